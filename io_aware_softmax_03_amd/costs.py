@@ -1,0 +1,92 @@
+"""Work and traffic accounting for the attention entry points (host-side arithmetic only).
+
+These are the conventions the bench reports against and the figures the pages
+derive on paper; tests pin each against the numbers the pages print.
+"""
+from __future__ import annotations
+
+import math
+
+
+def fwd_flops(B, H, N, d, causal):
+    """Forward FLOPs by convention: two products of 2*N*N*d each per head, halved when causal.
+
+    Per tile the two products cost 4*Br*Bc*d ("FlashAttention-2 and -3",
+    "Fewer non-matmul FLOPs" and "FlashAttention-3, built for asynchrony").
+    """
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def varlen_fwd_flops(lengths, H, d, causal):
+    """Packed forward: useful work is the sum of per-sequence squares ("Variable-length batches")."""
+    f = sum(4.0 * H * L * L * d for L in lengths)
+    return f / 2 if causal else f
+
+
+def bwd_flops(B, H, N, d, causal):
+    """Backward FLOPs by the stated convention: five products, 2.5x the forward."""
+    return 2.5 * fwd_flops(B, H, N, d, causal)
+
+
+def decode_flops(B, H, L, d):
+    return 4.0 * B * H * L * d
+
+
+def decode_bytes(B, H, L, d, elem_bytes=2):
+    """Compulsory HBM bytes of one decode step: K and V caches read once, plus q and o."""
+    return 2.0 * B * L * H * d * elem_bytes + 2.0 * B * H * d * elem_bytes
+
+
+def fwd_compulsory_bytes(B, H, N, d, elem_bytes=2):
+    """Q, K, V read once, O written once, fp32 LSE written once."""
+    return 4.0 * B * N * H * d * elem_bytes + 4.0 * B * H * N
+
+
+def fwd_grid_blocks(B, H, N, block_rows):
+    """FlashAttention-2 launch grid: (query blocks) x (batch * heads)
+    ("Parallelism over the sequence")."""
+    return math.ceil(N / block_rows) * B * H
+
+
+def fa1_grid_blocks(B, H):
+    """FlashAttention-1 launch grid: one block per (sequence, head) ("three leaks")."""
+    return B * H
+
+
+def idle_fraction(blocks, n_units):
+    """Fraction of compute units left idle when blocks < units, one block per unit."""
+    return max(0.0, 1.0 - blocks / n_units)
+
+
+def non_matmul_time_ratio(d, ops_per_score=5, penalty=16):
+    """Non-matmul time relative to matmul time per tile:
+    penalty * ops * Br*Bc / (4*Br*Bc*d) = penalty*ops/(4d)  ("Fewer non-matmul FLOPs")."""
+    return penalty * ops_per_score / (4.0 * d)
+
+
+def exp_to_matmul_time(d, matmul_rate, exp_rate):
+    """Time of the Br*Bc exponentials relative to the 4*Br*Bc*d matmul FLOPs of one tile,
+    each at its own unit's rate ("FlashAttention-3, built for asynchrony")."""
+    return (1.0 / exp_rate) / (4.0 * d / matmul_rate)
+
+
+def padded_and_useful_scores(lengths):
+    """Scores per head with padding to the longest sequence, and the useful ones."""
+    lengths = list(lengths)
+    return len(lengths) * max(lengths) ** 2, sum(L * L for L in lengths)
+
+
+def naive_score_matrix(n, elem_bytes=2):
+    """Entries and bytes of one n x n score matrix (naive attention materialises it)."""
+    return n * n, n * n * elem_bytes
+
+
+def causal_tiles_visited(n_rows, n_cols, block_rows, block_cols):
+    """Number of (query block, key block) tiles with at least one visible entry
+    under the top-left causal mask; tiles above the diagonal are skipped."""
+    count = 0
+    for i in range(math.ceil(n_rows / block_rows)):
+        last_row = min((i + 1) * block_rows, n_rows) - 1
+        count += min(math.ceil(n_cols / block_cols), last_row // block_cols + 1)
+    return count

@@ -1,0 +1,154 @@
+"""Exact attention written out from its definition, in float64 (test infrastructure only).
+
+Definition (FlashAttention: IO-aware exact attention, opening section, and
+"Flash Attention and the Online-Softmax Trick", §1): for one (batch, head)
+slice with queries q [Nq, d], keys k [Nk, d] and values v [Nk, dv],
+
+    S = scale * q k^T                       (Nq x Nk, materialised)
+    S[i, j] = -inf where masked             (causal: key j > query i)
+    m_i = max_j S_ij,  l_i = sum_j exp(S_ij - m_i)
+    P = exp(S - m) / l                      (rows sum to one)
+    O = P v,           LSE_i = m_i + ln l_i (natural log)
+
+The log-sum-exp output is the statistic FlashAttention-2 keeps for the backward
+pass ("FlashAttention-2 and -3" page, section "Fewer non-matmul FLOPs").
+
+Readings taken where the pages are silent (each is listed in the design notes):
+* ``scale`` multiplies q k^T before the softmax; LSE is the natural log of the
+  sum of exponentials of the *scaled* scores.
+* causal keeps key j for query i when j <= i, counted from the top-left
+  corner (the PyTorch ``is_causal`` alignment the "Using it, the real way"
+  section describes). For the square shapes used here top-left and
+  bottom-right coincide.
+* a row with every key masked has O = 0 and LSE = -inf.
+* the backward pass is the exact gradient of O(q, k, v) for an upstream dO,
+  derived by calculus from the definition above; the pages state only that it
+  recomputes the tiles from the saved LSE.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def _causal_keep(nq: int, nk: int) -> np.ndarray:
+    """Boolean [nq, nk] mask: key j is visible to query i when j <= i (top-left)."""
+    return np.arange(nk)[None, :] <= np.arange(nq)[:, None]
+
+
+def attention_head(q, k, v, scale, causal=False, return_p=False):
+    """Forward attention for one (batch, head) slice; returns (O, LSE[, P])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    S = float(scale) * (q @ k.T)
+    if causal:
+        S = np.where(_causal_keep(q.shape[0], k.shape[0]), S, -np.inf)
+    m = S.max(axis=1) if S.shape[1] else np.full(S.shape[0], -np.inf)
+    has_key = np.isfinite(m)
+    m_ref = np.where(has_key, m, 0.0)
+    E = np.exp(S - m_ref[:, None])          # exp(-inf) = 0 on masked entries
+    l = E.sum(axis=1)
+    P = E / np.where(l > 0, l, 1.0)[:, None]
+    O = P @ v
+    lse = np.where(l > 0, m_ref + np.log(np.where(l > 0, l, 1.0)), -np.inf)
+    if return_p:
+        return O, lse, P
+    return O, lse
+
+
+def attn_fwd(q, k, v, scale, causal=False):
+    """Dense forward. q, k, v: [B, N, H, d]. Returns O [B, N, H, d], LSE [B, H, N]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, N, H, _ = q.shape
+    O = np.empty(q.shape[:3] + (v.shape[3],))
+    lse = np.empty((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            O[b, :, h, :], lse[b, h, :] = attention_head(q[b, :, h], k[b, :, h], v[b, :, h],
+                                                         scale, causal)
+    return O, lse
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens, scale, causal=False):
+    """Packed variable-length forward ("Variable-length batches without padding").
+
+    q, k, v: [total_tokens, H, d]; sequence s occupies rows cu_seqlens[s] to
+    cu_seqlens[s+1]. Attention never crosses a sequence boundary (block-diagonal
+    document mask); causal is counted within each sequence.
+    Returns O [total_tokens, H, d] and LSE [H, total_tokens].
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    if cu.ndim != 1 or cu[0] != 0 or np.any(np.diff(cu) < 0) or cu[-1] != q.shape[0]:
+        raise ValueError("cu_seqlens must start at 0, be nondecreasing and end at total_tokens")
+    T, H, _ = q.shape
+    O = np.zeros((T, H, v.shape[2]))
+    lse = np.full((H, T), -np.inf)
+    for s in range(len(cu) - 1):
+        a, e = int(cu[s]), int(cu[s + 1])
+        if e == a:
+            continue
+        for h in range(H):
+            O[a:e, h, :], lse[h, a:e] = attention_head(q[a:e, h], k[a:e, h], v[a:e, h],
+                                                       scale, causal)
+    return O, lse
+
+
+def attn_bwd_head(q, k, v, do, scale, causal=False):
+    """Exact gradients for one slice. Returns dict with dq, dk, dv, o, lse, delta.
+
+    With P the forward probabilities and dO the upstream gradient of O:
+        dV = P^T dO
+        dP = dO v^T
+        D_i = sum_j P_ij dP_ij          (equals sum_c dO_ic O_ic)
+        dS = P * (dP - D)               (softmax Jacobian, row by row)
+        dQ = scale * dS k
+        dK = scale * dS^T q
+    Masked entries have P = 0 and contribute nothing.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    o, lse, P = attention_head(q, k, v, scale, causal, return_p=True)
+    dv = P.T @ do
+    dP = do @ v.T
+    delta = (P * dP).sum(axis=1)
+    dS = P * (dP - delta[:, None])
+    dq = float(scale) * (dS @ k)
+    dk = float(scale) * (dS.T @ q)
+    return {"dq": dq, "dk": dk, "dv": dv, "o": o, "lse": lse, "delta": delta}
+
+
+def attn_bwd(q, k, v, do, scale, causal=False):
+    """Dense backward. All tensors [B, N, H, d]; returns (dq, dk, dv) in float64."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, N, H, _ = q.shape
+    dq, dk, dv = np.empty(q.shape), np.empty(k.shape), np.empty(v.shape)
+    for b in range(B):
+        for h in range(H):
+            g = attn_bwd_head(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], scale, causal)
+            dq[b, :, h], dk[b, :, h], dv[b, :, h] = g["dq"], g["dk"], g["dv"]
+    return dq, dk, dv
+
+
+def attn_decode_slice(q_vec, k_rows, v_rows, scale):
+    """One decode step for one (batch, head): a single query against L cached keys.
+
+    The newest token sees every cached key, so there is no mask. Not split into
+    chunks: the split-and-merge of Flash-Decoding is checked separately.
+    Returns (o [dv], lse scalar).
+    """
+    o, lse = attention_head(_f64(q_vec)[None, :], k_rows, v_rows, scale, causal=False)
+    return o[0], float(lse[0])
+
+
+def attn_decode(q, k_cache, v_cache, scale):
+    """Decode for a batch. q [B, H, d]; caches [B, L, H, d]. Returns O [B, H, d], LSE [B, H]."""
+    q, kc, vc = _f64(q), _f64(k_cache), _f64(v_cache)
+    B, H, _ = q.shape
+    O = np.empty((B, H, vc.shape[3]))
+    lse = np.empty((B, H))
+    for b in range(B):
+        for h in range(H):
+            O[b, h], lse[b, h] = attn_decode_slice(q[b, h], kc[b, :, h], vc[b, :, h], scale)
+    return O, lse
