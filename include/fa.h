@@ -1,0 +1,155 @@
+/*
+ * fa.h — exact scaled-dot-product attention on MI355X (gfx950), FlashAttention style.
+ *
+ * What every call computes, per (batch, head):
+ *     S = scale * Q K^T,  P = softmax_rows(S)  (masked entries excluded),  O = P V,
+ *     LSE_i = ln sum_j exp(S_ij)               (natural log of the scaled scores)
+ * without ever writing an N x N matrix to device memory: query row-blocks are
+ * held on chip while key/value column-blocks stream past, and the softmax is
+ * carried online (running maximum, running sum, unnormalised output rescaled
+ * when the maximum moves, one division at the end).
+ *   Definitions: "FlashAttention: IO-aware exact attention", sections
+ *   "Tile decomposition" and "Online softmax"; "FlashAttention-2 and -3"
+ *   (efficient-attention/flash-2-3), section "Fewer non-matmul FLOPs"
+ *   (unnormalised accumulator, log-sum-exp kept for the backward pass).
+ *
+ * Conventions shared by every entry point
+ *   Layout   Q, K, V, O, dO, dQ, dK, dV are contiguous [B, N, H, d] (the
+ *            (batch, T, heads, d) layout of the flash-attn package, "Flash
+ *            Attention and the Online-Softmax Trick" §7). Packed variable-length
+ *            tensors are [total_tokens, H, d]. LSE is fp32 [B, H, N]
+ *            ([H, total_tokens] for varlen, [B, H] for decode).
+ *   Causal   query i sees key j when j <= i, both counted from the start of
+ *            the sequence. For the square shapes accepted here this is both the
+ *            top-left and the bottom-right alignment described in
+ *            "FlashAttention-2 and -3", section "Using it, the real way".
+ *   Scale    multiplies Q K^T before the softmax; callers normally pass
+ *            1/sqrt(d). Must be finite and > 0.
+ *   dtype    FA_DTYPE_BF16: bf16 inputs, fp32 accumulation, O rounded once to
+ *            bf16 (round to nearest even). FA_DTYPE_F32: fp32 throughout.
+ *   Head dim d must be 64 or 128.
+ *   Memory   every pointer is device memory owned by the caller; the library
+ *            allocates nothing and keeps no state between calls. Workspaces
+ *            are passed in after a size query.
+ *   Streams  `stream` is a hipStream_t (NULL = the default stream). Calls only
+ *            enqueue kernels on that stream: no host synchronisation and no
+ *            device-to-host copy. Results are ready when the stream is.
+ *   Errors   arguments are checked on the host before any HIP call, so a bad
+ *            call returns an error code without touching the device; there is
+ *            never a fallback to another algorithm ("Using it, the real way":
+ *            ask for the fused kernel and get an error rather than a slower
+ *            path). A failed kernel launch returns FA_ERR_HIP.
+ *   Sizes    element counts of every tensor must fit in int64; per-sequence
+ *            lengths fit in int32.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,      /* a required pointer is NULL */
+  FA_ERR_SHAPE = -2,     /* a size is <= 0, too large, or inconsistent */
+  FA_ERR_HEADDIM = -3,   /* d is not supported (supported: 64, 128) */
+  FA_ERR_DTYPE = -4,     /* dtype not supported by this entry point */
+  FA_ERR_WORKSPACE = -5, /* workspace missing or smaller than the size query returned */
+  FA_ERR_ARG = -6,       /* other invalid argument (scale, num_splits, flags) */
+  FA_ERR_HIP = -7        /* the HIP runtime reported an error launching a kernel */
+} fa_status;
+
+typedef enum { FA_DTYPE_F32 = 0, FA_DTYPE_BF16 = 1 } fa_dtype;
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char* fa_strerror(int status);
+
+/*
+ * fa_fwd — dense forward.
+ *   q, k, v  [B, N, H, d] of `dtype` (read only)
+ *   o        [B, N, H, d] of `dtype` (written)
+ *   lse      fp32 [B, H, N] (written): LSE_i = m_i + ln l_i, kept for fa_bwd
+ *            ("Fewer non-matmul FLOPs"). May not be NULL.
+ *   causal   0 or 1.
+ * Key/value blocks that lie entirely above the causal diagonal are never
+ * visited ("Fewer non-matmul FLOPs": skipping the masked causal tiles). The
+ * launch grid is (query blocks) x (batch * heads) ("Parallelism over the
+ * sequence").
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_fwd_varlen — forward over sequences packed end to end without padding
+ * ("FlashAttention-2 and -3", section "Variable-length batches without padding").
+ *   q, k, v, o   [total_tokens, H, d]
+ *   lse          fp32 [H, total_tokens]
+ *   cu_seqlens   device int32 [num_seqs + 1]: cu_seqlens[0] = 0, nondecreasing,
+ *                cu_seqlens[num_seqs] = total_tokens. Sequence s occupies rows
+ *                cu_seqlens[s] .. cu_seqlens[s+1]-1. The contents are the
+ *                caller's contract (they live on the device and are not read by
+ *                the host); rows of a sequence longer than max_seqlen are not
+ *                written.
+ *   max_seqlen   >= every sequence length; sizes the launch grid.
+ * Attention never crosses a sequence boundary (block-diagonal mask); causal is
+ * counted within each sequence. Empty sequences are allowed.
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int* cu_seqlens, int num_seqs, int total_tokens, int max_seqlen,
+                  int H, int d, float scale, int causal, int dtype, void* stream);
+
+/* Bytes of workspace fa_bwd needs: the row statistic D = rowsum(dO * O), fp32 [B, H, N]. */
+size_t fa_bwd_workspace_bytes(int B, int H, int N);
+
+/*
+ * fa_bwd — backward by recomputation ("FlashAttention: IO-aware exact
+ * attention", "Tile decomposition", last paragraph; "FlashAttention-2 and -3",
+ * "Parallelism over the sequence", last paragraph).
+ *   q, k, v, dout   [B, N, H, d] bf16, the forward's inputs and the upstream gradient
+ *   o, lse          the forward's outputs for the same inputs (fa_fwd)
+ *   dq, dk, dv      fp32 [B, N, H, d] (written). dq is cleared by the call and then
+ *                   accumulated with device atomics; dk, dv are written once per
+ *                   key block.
+ *   workspace       >= fa_bwd_workspace_bytes(B, H, N) bytes of device memory.
+ * Probabilities are recomputed from Q, K and the saved LSE as exp(s - LSE); the
+ * gradient is dV = P^T dO, dS = P * (dO V^T - D), dQ = scale dS K, dK = scale dS^T Q.
+ * Only FA_DTYPE_BF16 is accepted. The order of the dq atomic additions varies
+ * from run to run, so dq is reproducible to rounding, not bit for bit.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, float* dq, float* dk, float* dv,
+           int B, int H, int N, int d, float scale, int causal, int dtype,
+           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace fa_decode needs for `num_splits` partials per (batch, head):
+ * fp32 running max, running sum and a d-wide partial output for each. */
+size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits);
+
+/*
+ * fa_decode — one query token per (batch, head) against a contiguous KV cache,
+ * split over the keys (Flash-Decoding; "FlashAttention-2 and -3", section
+ * "Decoding needs a different split").
+ *   q          [B, H, d]
+ *   k_cache,
+ *   v_cache    [B, L, H, d]
+ *   o          [B, H, d] (written)
+ *   lse        fp32 [B, H] (written) or NULL
+ *   num_splits 1 .. 1024 chunks of ceil(L / num_splits) keys. Each chunk yields
+ *              its running max, sum and partial output; a second small kernel
+ *              merges them with log-sum-exp weights (each chunk weighted by its
+ *              softmax mass). The merged result does not depend on num_splits
+ *              beyond rounding.
+ * The new token sees every cached key (no mask). Only FA_DTYPE_BF16.
+ */
+int fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+              int B, int H, int L, int d, float scale, int num_splits, int dtype,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

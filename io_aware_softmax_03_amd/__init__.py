@@ -1,1 +1,128 @@
-"""MI355X-native exact attention: tiled online-softmax kernels behind a C ABI."""
+"""MI355X-native exact attention: tiled online-softmax HIP kernels behind a C ABI.
+
+Python entry points with the same names as the C calls. They only marshal
+arguments (device pointers, sizes, the current HIP stream); every step of the
+computation runs in the HIP kernels of ``libfa.so``. PyTorch provides device
+memory and streams. Tensors must be contiguous device tensors:
+
+    fwd(q, k, v, scale=None, causal=False) -> (o, lse)          q,k,v [B, N, H, d]
+    fwd_varlen(q, k, v, cu_seqlens, max_seqlen, ...) -> (o, lse) q,k,v [T, H, d]
+    bwd(q, k, v, o, lse, do, scale=None, causal=False) -> (dq, dk, dv)   fp32 grads
+    decode(q, k_cache, v_cache, scale=None, num_splits=64) -> (o, lse)   q [B, H, d]
+
+``scale`` defaults to 1/sqrt(d).
+"""
+from __future__ import annotations
+
+import math
+
+from ._clib import (  # noqa: F401
+    FAError, FA_DTYPE_BF16, FA_DTYPE_F32, check, lib, strerror,
+)
+
+__all__ = ["fwd", "fwd_varlen", "bwd", "decode", "FAError", "lib"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return FA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return FA_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _require(tensors, names):
+    for t, n in zip(tensors, names):
+        if not t.is_cuda:
+            raise ValueError(f"{n} must be a GPU tensor (no CPU path exists)")
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+
+
+def _stream(device):
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _scale(scale, d):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def fwd(q, k, v, scale=None, causal=False):
+    """Dense forward. Returns O (q's dtype, [B, N, H, d]) and fp32 LSE [B, H, N]."""
+    torch = _torch()
+    _require((q, k, v), ("q", "k", "v"))
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must all be [B, N, H, d]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    B, N, H, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = lib().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                      B, H, N, d, _scale(scale, d), int(bool(causal)), _dtype_code(q), _stream(q.device))
+    check(st, "fa_fwd")
+    return o, lse
+
+
+def fwd_varlen(q, k, v, cu_seqlens, max_seqlen, scale=None, causal=False):
+    """Packed forward over sequences laid end to end. q, k, v: [T, H, d]; cu_seqlens: int32
+    device tensor [num_seqs + 1]; max_seqlen: the longest sequence length (host int).
+    Returns O [T, H, d] and fp32 LSE [H, T]."""
+    torch = _torch()
+    _require((q, k, v, cu_seqlens), ("q", "k", "v", "cu_seqlens"))
+    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must all be [total_tokens, H, d]")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise TypeError("cu_seqlens must be a 1-D int32 tensor")
+    T, H, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    st = lib().fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                             cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, T, int(max_seqlen), H, d,
+                             _scale(scale, d), int(bool(causal)), _dtype_code(q), _stream(q.device))
+    check(st, "fa_fwd_varlen")
+    return o, lse
+
+
+def bwd(q, k, v, o, lse, do, scale=None, causal=False):
+    """Backward from the forward's O and LSE. Returns fp32 dq, dk, dv [B, N, H, d]."""
+    torch = _torch()
+    _require((q, k, v, o, lse, do), ("q", "k", "v", "o", "lse", "do"))
+    B, N, H, d = q.shape
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    nbytes = lib().fa_bwd_workspace_bytes(B, H, N)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    st = lib().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, _scale(scale, d),
+                      int(bool(causal)), _dtype_code(q), ws.data_ptr(), ws.numel(), _stream(q.device))
+    check(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def decode(q, k_cache, v_cache, scale=None, num_splits=64, workspace=None):
+    """Single-token decode. q [B, H, d]; caches [B, L, H, d]. Returns O [B, H, d], LSE [B, H]."""
+    torch = _torch()
+    _require((q, k_cache, v_cache), ("q", "k_cache", "v_cache"))
+    B, H, d = q.shape
+    L = k_cache.shape[1]
+    if k_cache.shape != (B, L, H, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [B, L, H, d] matching q")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    nbytes = lib().fa_decode_workspace_bytes(B, H, d, num_splits)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    st = lib().fa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                         B, H, L, d, _scale(scale, d), num_splits, _dtype_code(q),
+                         workspace.data_ptr(), workspace.numel(), _stream(q.device))
+    check(st, "fa_decode")
+    return o, lse

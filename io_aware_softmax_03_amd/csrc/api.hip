@@ -1,0 +1,126 @@
+// C ABI of the attention library: argument validation on the host, then kernel launches
+// on the caller's stream. Every check happens before the first HIP call, so invalid calls
+// return an error code without touching the device; there is no fallback path.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_launch.hpp"
+
+namespace {
+
+constexpr long long kMaxElems = 1LL << 62;
+constexpr int kMaxSplits = 1024;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
+
+int fits(long long a, long long b, long long c, long long d) {
+  // a*b*c*d <= kMaxElems for non-negative factors
+  long long x = a;
+  for (long long f : {b, c, d}) {
+    if (f != 0 && x > kMaxElems / f) return 0;
+    x *= f;
+  }
+  return 1;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case FA_ERR_HEADDIM: return "unsupported head dimension (supported: 64, 128)";
+    case FA_ERR_DTYPE: return "unsupported dtype for this entry point";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_ARG: return "invalid argument (scale, flag, split count or pointer alignment)";
+    case FA_ERR_HIP: return "HIP runtime error while launching a kernel";
+    default: return "unknown status";
+  }
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+           int d, float scale, int causal, int dtype, void* stream) {
+  if (B < 0 || N < 0 || H <= 0) return FA_ERR_SHAPE;
+  if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32) return FA_ERR_DTYPE;
+  if (!scale_ok(scale) || (causal != 0 && causal != 1)) return FA_ERR_ARG;
+  if (!fits(B, N, H, d)) return FA_ERR_SHAPE;
+  if (B == 0 || N == 0) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ARG;
+  fa::FwdArgs a{q, k, v, o, lse, nullptr, B, H, N, N, d, scale, causal != 0};
+  hipStream_t s = (hipStream_t)stream;
+  return from_hip(dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(a, s) : fa::launch_fwd_f32(a, s));
+}
+
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens,
+                  int num_seqs, int total_tokens, int max_seqlen, int H, int d, float scale, int causal,
+                  int dtype, void* stream) {
+  if (num_seqs < 0 || total_tokens < 0 || max_seqlen < 0 || H <= 0) return FA_ERR_SHAPE;
+  if (max_seqlen > total_tokens) return FA_ERR_SHAPE;
+  if (total_tokens > 0 && (max_seqlen == 0 || num_seqs == 0)) return FA_ERR_SHAPE;
+  if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32) return FA_ERR_DTYPE;
+  if (!scale_ok(scale) || (causal != 0 && causal != 1)) return FA_ERR_ARG;
+  if (!fits(total_tokens, H, d, 1)) return FA_ERR_SHAPE;
+  if (total_tokens == 0) return FA_OK;
+  if (!q || !k || !v || !o || !lse || !cu_seqlens) return FA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ARG;
+  fa::FwdArgs a{q, k, v, o, lse, cu_seqlens, num_seqs, H, max_seqlen, total_tokens, d, scale, causal != 0};
+  hipStream_t s = (hipStream_t)stream;
+  return from_hip(dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(a, s) : fa::launch_fwd_f32(a, s));
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N) {
+  if (B < 0 || H < 0 || N < 0) return 0;
+  return (size_t)B * H * N * sizeof(float);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+           float* dq, float* dk, float* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
+           void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || N < 0 || H <= 0) return FA_ERR_SHAPE;
+  if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (!scale_ok(scale) || (causal != 0 && causal != 1)) return FA_ERR_ARG;
+  if (!fits(B, N, H, d)) return FA_ERR_SHAPE;
+  if (B == 0 || N == 0) return FA_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, H, N)) return FA_ERR_WORKSPACE;
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ARG;
+  fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, (float*)workspace, B, H, N, d, scale, causal != 0};
+  return from_hip(fa::launch_bwd_bf16(a, (hipStream_t)stream));
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits) {
+  if (B < 0 || H < 0 || d < 0 || num_splits < 0) return 0;
+  return (size_t)B * H * num_splits * (d + 2) * sizeof(float);
+}
+
+int fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B, int H, int L,
+              int d, float scale, int num_splits, int dtype, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  if (B < 0 || H <= 0 || L <= 0) return FA_ERR_SHAPE;
+  if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (!scale_ok(scale) || num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_ARG;
+  if (!fits(B, L, H, d)) return FA_ERR_SHAPE;
+  if (B == 0) return FA_OK;
+  if (!q || !k_cache || !v_cache || !o) return FA_ERR_NULL;
+  if (!workspace || workspace_bytes < fa_decode_workspace_bytes(B, H, d, num_splits)) return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace)) return FA_ERR_ARG;
+  fa::DecodeArgs a{q, k_cache, v_cache, o, lse, (float*)workspace, B, H, L, d, num_splits, scale};
+  return from_hip(fa::launch_decode_bf16(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

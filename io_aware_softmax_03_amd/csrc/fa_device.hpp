@@ -1,0 +1,83 @@
+// Device-side building blocks shared by the gfx950 attention kernels.
+//
+// Lane layouts used throughout (wave64, lane l, r = l & 31, half = l >> 5):
+//   v_mfma_f32_32x32x16_bf16  A (32 x 16): lane holds A[r][8*half .. 8*half+7]
+//                             B (16 x 32): lane holds B[8*half .. 8*half+7][r]
+//                             C (32 x 32): lane holds C[8*i + 4*half + j][r] at acc[4*i + j]
+//   ds_read_b64_tr_b16        within each group of 16 lanes, output lane j element e is
+//                             element (j & 3) of what input lane 4*e + (j >> 2) addressed:
+//                             if input lane i reads row (base + i/4), columns
+//                             (col + 4*(i%4) .. +3) of a row-major bf16 tile, output lane j
+//                             receives column (col + j) of rows base .. base+3.
+//   v_permlane32_swap         with both operands equal to x, the two results hold
+//                             x[l & 31] and x[(l & 31) + 32].
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value held by the lane 32 positions away (the other half of the wave).
+__device__ __forceinline__ float pair_max(float x) {
+  auto s = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float(s[0]), __int_as_float(s[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto s = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(s[0]) + __int_as_float(s[1]);
+}
+
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// Round-to-nearest-even fp32 -> bf16 of two values, packed low/high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3,
+                                              float a4, float a5, float a6, float a7) {
+  u32x4 w;
+  w[0] = pack_bf16x2(a0, a1);
+  w[1] = pack_bf16x2(a2, a3);
+  w[2] = pack_bf16x2(a4, a5);
+  w[3] = pack_bf16x2(a6, a7);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Transposing 8-byte LDS read (see the layout note at the top of this file).
+__device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_u16*)p);
+}
+
+__device__ __forceinline__ bf16x8 join_tr(const i16x4& lo, const i16x4& hi) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, x);
+}
+
+}  // namespace fa

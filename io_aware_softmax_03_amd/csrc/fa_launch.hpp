@@ -1,0 +1,59 @@
+// Host-side launch functions implemented in the kernel sources and called by the C ABI
+// after argument validation. Each returns hipSuccess or the launch error.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int* cu_seqlens;  // NULL for the dense [B, N, H, d] layout
+  int batch;              // dense: B; packed: number of sequences
+  int heads;
+  int seqlen;             // dense: N; packed: max_seqlen (sizes the grid)
+  int total_rows;         // dense: N; packed: total_tokens (LSE row stride)
+  int head_dim;
+  float scale;
+  bool causal;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* delta;  // workspace, [B, H, N]
+  int batch, heads, seqlen, head_dim;
+  float scale;
+  bool causal;
+};
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  void* o;
+  float* lse;       // may be NULL
+  float* partials;  // workspace: [B, H, S] max, [B, H, S] sum, [B, H, S, d] output
+  int batch, heads, cache_len, head_dim, num_splits;
+  float scale;
+};
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,157 @@
+// Forward attention in fp32 throughout (inputs, products, softmax, output).
+//
+// The exact-precision path: same tiled online softmax as the bf16 kernel ("Tile
+// decomposition", "Online softmax"), but the products use fp32 FMAs rather than reduced
+// precision matrix cores, so results stay within fp32 rounding of the exact value.
+// Each query row is owned by D/32 consecutive lanes (32 head dims each); K and V blocks of
+// 32 keys are staged in LDS and read as broadcasts.
+#include "fa_device.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+namespace {
+
+constexpr int kKT = 32;     // keys per block
+constexpr int kThreads = 256;
+
+struct F32Args {
+  const float* q;
+  const float* k;
+  const float* v;
+  float* o;
+  float* lse;
+  const int* cu_seqlens;
+  int heads, seqlen, total_rows, nqb;
+  float scale_log2;
+};
+
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args p) {
+  constexpr int TPR = D / 32;            // lanes per query row
+  constexpr int RPB = kThreads / TPR;    // query rows per workgroup
+  __shared__ __attribute__((aligned(16))) float ks[kKT * D];
+  __shared__ __attribute__((aligned(16))) float vs[kKT * D];
+
+  const int qb = p.nqb - 1 - (int)(blockIdx.x % p.nqb);
+  const int bh = blockIdx.x / p.nqb;
+  const int h = bh % p.heads, bs = bh / p.heads;
+  int seq_start, L;
+  if constexpr (VARLEN) {
+    seq_start = p.cu_seqlens[bs];
+    L = p.cu_seqlens[bs + 1] - seq_start;
+  } else {
+    seq_start = bs * p.seqlen;
+    L = p.seqlen;
+  }
+  const int q0 = qb * RPB;
+  if (q0 >= L) return;
+  const size_t rs = (size_t)p.heads * D;
+  const size_t base = ((size_t)seq_start * p.heads + h) * D;
+  const int tid = threadIdx.x;
+  const int part = tid % TPR;
+  const int myq = q0 + tid / TPR;
+  const bool valid = myq < L;
+
+  float qv[32], ov[32];
+#pragma unroll
+  for (int c = 0; c < 32; ++c) {
+    qv[c] = valid ? p.q[base + (size_t)myq * rs + part * 32 + c] : 0.f;
+    ov[c] = 0.f;
+  }
+  float m = -1e30f, l = 0.f;
+
+  int kv_end = L;
+  if constexpr (CAUSAL) kv_end = min(L, q0 + RPB);
+  for (int k0 = 0; k0 < kv_end; k0 += kKT) {
+    __syncthreads();
+    for (int e = tid; e < kKT * D; e += kThreads) {
+      const int row = e / D, col = e % D;
+      const int key = k0 + row;
+      const bool in = key < L;
+      ks[e] = in ? p.k[base + (size_t)key * rs + col] : 0.f;
+      vs[e] = in ? p.v[base + (size_t)key * rs + col] : 0.f;
+    }
+    __syncthreads();
+    float s[kKT];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kKT; ++j) {
+      float acc = 0.f;
+#pragma unroll
+      for (int c = 0; c < 32; ++c) acc = __builtin_fmaf(qv[c], ks[j * D + part * 32 + c], acc);
+#pragma unroll
+      for (int off = 1; off < TPR; off <<= 1) acc += __shfl_xor(acc, off);
+      const int key = k0 + j;
+      const bool keep = key < L && (!CAUSAL || key <= myq);
+      s[j] = keep ? acc * p.scale_log2 : -INFINITY;
+      mt = fmaxf(mt, s[j]);
+    }
+    const float m_new = fmaxf(m, mt);
+    const float alpha = exp2_fast(m - m_new);
+    float ls = 0.f;
+#pragma unroll
+    for (int j = 0; j < kKT; ++j) {
+      s[j] = exp2_fast(s[j] - m_new);
+      ls += s[j];
+    }
+    l = l * alpha + ls;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      float acc = ov[c] * alpha;
+#pragma unroll
+      for (int j = 0; j < kKT; ++j) acc = __builtin_fmaf(s[j], vs[j * D + part * 32 + c], acc);
+      ov[c] = acc;
+    }
+    m = m_new;
+  }
+  if (!valid) return;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+  for (int c = 0; c < 32; ++c) p.o[base + (size_t)myq * rs + part * 32 + c] = ov[c] * inv;
+  if (part == 0) {
+    const float lse = l > 0.f ? (m + log2_fast(l)) * kLn2 : -INFINITY;
+    if constexpr (VARLEN)
+      p.lse[(size_t)h * p.total_rows + seq_start + myq] = lse;
+    else
+      p.lse[((size_t)bs * p.heads + h) * p.seqlen + myq] = lse;
+  }
+}
+
+template <int D, bool CAUSAL, bool VARLEN>
+hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
+  constexpr int RPB = kThreads / (D / 32);
+  F32Args p;
+  p.q = (const float*)a.q;
+  p.k = (const float*)a.k;
+  p.v = (const float*)a.v;
+  p.o = (float*)a.o;
+  p.lse = a.lse;
+  p.cu_seqlens = a.cu_seqlens;
+  p.heads = a.heads;
+  p.seqlen = a.seqlen;
+  p.total_rows = a.total_rows;
+  p.nqb = (a.seqlen + RPB - 1) / RPB;
+  p.scale_log2 = a.scale * kLog2e;
+  const long long blocks = (long long)p.nqb * a.heads * a.batch;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
+  const bool varlen = a.cu_seqlens != nullptr;
+  if (a.causal) return varlen ? launch_t<D, true, true>(a, stream) : launch_t<D, true, false>(a, stream);
+  return varlen ? launch_t<D, false, true>(a, stream) : launch_t<D, false, false>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream) {
+  if (a.head_dim == 128) return launch_d<128>(a, stream);
+  if (a.head_dim == 64) return launch_d<64>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa
