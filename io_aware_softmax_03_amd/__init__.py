@@ -54,8 +54,9 @@ def _scale(scale, d):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
-def fwd(q, k, v, scale=None, causal=False):
-    """Dense forward. Returns O (q's dtype, [B, N, H, d]) and fp32 LSE [B, H, N]."""
+def fwd(q, k, v, scale=None, causal=False, out=None):
+    """Dense forward. Returns O (q's dtype, [B, N, H, d]) and fp32 LSE [B, H, N].
+    ``out=(o, lse)`` writes into preallocated tensors of those shapes."""
     torch = _torch()
     _require((q, k, v), ("q", "k", "v"))
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
@@ -63,8 +64,14 @@ def fwd(q, k, v, scale=None, causal=False):
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share a dtype")
     B, N, H, d = q.shape
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        _require((o, lse), ("o", "lse"))
+        if o.shape != q.shape or o.dtype != q.dtype or lse.shape != (B, H, N) or lse.dtype != torch.float32:
+            raise ValueError("out must be (o [B, N, H, d] like q, lse fp32 [B, H, N])")
     st = lib().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                       B, H, N, d, _scale(scale, d), int(bool(causal)), _dtype_code(q), _stream(q.device))
     check(st, "fa_fwd")
@@ -91,16 +98,31 @@ def fwd_varlen(q, k, v, cu_seqlens, max_seqlen, scale=None, causal=False):
     return o, lse
 
 
-def bwd(q, k, v, o, lse, do, scale=None, causal=False):
-    """Backward from the forward's O and LSE. Returns fp32 dq, dk, dv [B, N, H, d]."""
+def bwd(q, k, v, o, lse, do, scale=None, causal=False, out=None, workspace=None):
+    """Backward from the forward's O and LSE. Returns fp32 dq, dk, dv [B, N, H, d].
+    ``out=(dq, dk, dv)`` and ``workspace`` may be preallocated."""
     torch = _torch()
     _require((q, k, v, o, lse, do), ("q", "k", "v", "o", "lse", "do"))
     B, N, H, d = q.shape
-    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    dk = torch.empty_like(dq)
-    dv = torch.empty_like(dq)
+    for t, n in ((k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{n} must match q in shape and dtype")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be fp32 [B, H, N]")
+    if out is None:
+        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        dk = torch.empty_like(dq)
+        dv = torch.empty_like(dq)
+    else:
+        dq, dk, dv = out
+        _require((dq, dk, dv), ("dq", "dk", "dv"))
+        for t in (dq, dk, dv):
+            if t.shape != q.shape or t.dtype != torch.float32:
+                raise ValueError("out gradients must be fp32 and shaped like q")
     nbytes = lib().fa_bwd_workspace_bytes(B, H, N)
-    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    ws = workspace
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     st = lib().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, _scale(scale, d),
                       int(bool(causal)), _dtype_code(q), ws.data_ptr(), ws.numel(), _stream(q.device))
@@ -108,7 +130,7 @@ def bwd(q, k, v, o, lse, do, scale=None, causal=False):
     return dq, dk, dv
 
 
-def decode(q, k_cache, v_cache, scale=None, num_splits=64, workspace=None):
+def decode(q, k_cache, v_cache, scale=None, num_splits=64, workspace=None, out=None):
     """Single-token decode. q [B, H, d]; caches [B, L, H, d]. Returns O [B, H, d], LSE [B, H]."""
     torch = _torch()
     _require((q, k_cache, v_cache), ("q", "k_cache", "v_cache"))
@@ -116,8 +138,16 @@ def decode(q, k_cache, v_cache, scale=None, num_splits=64, workspace=None):
     L = k_cache.shape[1]
     if k_cache.shape != (B, L, H, d) or v_cache.shape != k_cache.shape:
         raise ValueError("caches must be [B, L, H, d] matching q")
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share a dtype")
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        _require((o, lse), ("o", "lse"))
+        if o.shape != q.shape or o.dtype != q.dtype or lse.shape != (B, H) or lse.dtype != torch.float32:
+            raise ValueError("out must be (o [B, H, d] like q, lse fp32 [B, H])")
     nbytes = lib().fa_decode_workspace_bytes(B, H, d, num_splits)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)

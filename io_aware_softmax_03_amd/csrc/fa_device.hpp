@@ -50,20 +50,40 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
-// Round-to-nearest-even fp32 -> bf16 of two values, packed low/high.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even fp32 -> bf16 of two values (one v_cvt_pk_bf16_f32), lo first.
+__device__ __forceinline__ bf16x2 cvt_bf16x2(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {lo, hi};
+  return __builtin_convertvector(v, bf16x2);
+}
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, cvt_bf16x2(lo, hi));
+}
+
+// Eight fp32 values -> bf16x8 MFMA operand; `sum` accumulates the eight *rounded* values
+// (v_dot2_f32_bf16 of each pair against (1, 1)), i.e. exactly the weights the MFMA uses.
+__device__ __forceinline__ bf16x8 pack_bf16x8_sum(const float* a, float& sum) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  const bf16x2 p0 = cvt_bf16x2(a[0], a[1]);
+  const bf16x2 p1 = cvt_bf16x2(a[2], a[3]);
+  const bf16x2 p2 = cvt_bf16x2(a[4], a[5]);
+  const bf16x2 p3 = cvt_bf16x2(a[6], a[7]);
+  sum = __builtin_amdgcn_fdot2_f32_bf16(p0, ones, sum, false);
+  sum = __builtin_amdgcn_fdot2_f32_bf16(p1, ones, sum, false);
+  sum = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, sum, false);
+  sum = __builtin_amdgcn_fdot2_f32_bf16(p3, ones, sum, false);
+  return __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
+                                 __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3,
                                               float a4, float a5, float a6, float a7) {
-  u32x4 w;
-  w[0] = pack_bf16x2(a0, a1);
-  w[1] = pack_bf16x2(a2, a3);
-  w[2] = pack_bf16x2(a4, a5);
-  w[3] = pack_bf16x2(a6, a7);
-  return __builtin_bit_cast(bf16x8, w);
+  const bf16x2 p0 = cvt_bf16x2(a0, a1), p1 = cvt_bf16x2(a2, a3);
+  const bf16x2 p2 = cvt_bf16x2(a4, a5), p3 = cvt_bf16x2(a6, a7);
+  return __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
+                                 __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

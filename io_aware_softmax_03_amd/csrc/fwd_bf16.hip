@@ -144,7 +144,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKernelArgs p) {
   };
 
   float m_ref = -1e30f;  // pivot (log2 units of scaled score), shared by both wave halves
-  float l_part = 0.f;    // this lane's half of the running sum
+  float l_part = 0.f;    // this lane's half of the running sum of P (fp32, for the LSE)
+  float lr_part = 0.f;   // the same sum over P as rounded to bf16 for the MFMA (normalises O)
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -203,6 +204,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKernelArgs p) {
         const float m_new = fmaxf(m_ref, mt);
         const float alpha = exp2_fast(m_ref - m_new);
         l_part *= alpha;
+        lr_part *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -226,8 +228,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKernelArgs p) {
         if (ks >= 2 && !need1) break;
         const f32x16& sp = (ks < 2) ? s0 : s1;
         const int o8 = 8 * (ks & 1);
-        const bf16x8 pb = pack_bf16x8(sp[o8 + 0], sp[o8 + 1], sp[o8 + 2], sp[o8 + 3],
-                                      sp[o8 + 4], sp[o8 + 5], sp[o8 + 6], sp[o8 + 7]);
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = sp[o8 + e];
+        const bf16x8 pb = pack_bf16x8_sum(pv, lr_part);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const int col = db * 32 + 16 * nh + 4 * (gi & 3);
@@ -245,8 +249,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKernelArgs p) {
 
   // ---- epilogue: one division by l, single bf16 rounding, natural-log LSE
   if (!wave_active) return;
+  // O is normalised by the sum of the weights it was accumulated with (bf16-rounded P), so
+  // the output is an exact convex combination of the rounded weights; the LSE uses the
+  // unrounded sum.
   const float l_tot = pair_sum(l_part);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lr_tot = pair_sum(lr_part);
+  const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
   if (myq < L) {
     uint16_t* og = p.o + base + (size_t)myq * rs;
 #pragma unroll
