@@ -180,6 +180,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (untimed), so that a counter "
+                         "profile of this command holds a kernel of known traffic to scale HBM counters by")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this library has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -189,6 +192,15 @@ def main():
     import torch
     import io_aware_softmax_03_amd as fa
     from io_aware_softmax_03_amd import costs
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: {n} bytes read, {n} bytes written")
+        del src, dst
 
     B, H, N, d = 2, 16, 8192, 128
     log(f"[bench] headline: causal bf16 forward B={B} H={H} N={N} d={d}")
