@@ -17,6 +17,10 @@
 //     "And on Blackwell"), so most blocks skip the accumulator rescale;
 //   * key blocks entirely above the causal diagonal are never loaded; within a block, a
 //     wave skips 32-key halves its rows cannot see.
+// gfx950 specifics: K and V tiles go from global memory straight into LDS
+// (global_load_lds_dwordx4, lane i -> bytes 16i of a wave's 1 KB slice), each lane picking
+// the source chunk that lands it at its swizzled position; every LDS operand address is a
+// per-lane register plus an immediate, and switching buffers flips one bit of those registers.
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -25,6 +29,9 @@ namespace {
 
 constexpr int kBC = 64;                    // keys per streamed block
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: P stays <= 256
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glob_void;
 
 struct FwdKernelArgs {
   const uint16_t* q;
@@ -40,30 +47,38 @@ struct FwdKernelArgs {
   float scale_log2;
 };
 
-// XOR swizzles of 16-byte chunks inside a tile row, chosen so that the MFMA operand reads
-// (K: 32 rows at one chunk; V: 8 rows x 4 chunks through the transpose read) and the
-// row-wise staging writes spread over all LDS banks.
+// XOR swizzles of 16-byte chunks inside a tile row. K is read 32 rows x one chunk per
+// ds_read_b128 (16 lanes = 16 consecutive rows must hit distinct chunks); V is read by the
+// transpose read, 8 rows x 4 chunks per instruction, 32 lanes covering 4 rows (the row's
+// two low bits must move the chunk's two high bits). Both keep row-wise fills conflict-free.
 template <int D>
 __device__ __forceinline__ int swz_k(int row) {
   return D == 128 ? (row & 15) : ((row >> 1) & 7);
 }
 template <int D>
 __device__ __forceinline__ int swz_v(int row) {
-  return D == 128 ? ((row & 7) << 1) : (((row >> 1) & 3) << 1);
+  return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
+
+__device__ __forceinline__ void copy16_to_lds(const uint16_t* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((glob_void*)src, (lds_void*)lds_wave_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
 template <int D, int NW, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKernelArgs p) {
-  constexpr int NT = NW * 64;
   constexpr int BR = 32 * NW;
-  constexpr int CH = D / 8;               // 16-byte chunks per row
-  constexpr int KK = D / 16;              // MFMA k-steps over the head dim
-  constexpr int DB = D / 32;              // 32-wide output blocks over the head dim
-  constexpr int TILE = kBC * D;           // elements per K or V tile
-  constexpr int LOADS = kBC * CH / NT;    // 16-byte chunks per thread per tile
-  static_assert(kBC * CH % NT == 0, "tile must split evenly over threads");
+  constexpr int CH = D / 8;                 // 16-byte chunks per row
+  constexpr int KK = D / 16;                // MFMA k-steps over the head dim
+  constexpr int DB = D / 32;                // 32-wide output blocks over the head dim
+  constexpr int TILE_B = kBC * D * 2;       // bytes of one K or V tile
+  constexpr int ROWS_PER_KB = 1024 / (2 * D);
+  constexpr int LOADS = TILE_B / 1024 / NW; // 1 KB wave-loads per tile per wave
+  static_assert(TILE_B % (1024 * NW) == 0, "tile must split evenly over waves");
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];  // K[2], V[2]
+  // [K buf0 | K buf1 | V buf0 | V buf1]
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_B];
 
   // ---- work decode: XCD-aware remap, heavy (late) query blocks first
   const int total = gridDim.x;
@@ -85,11 +100,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKernelArgs p) {
   if (q0 >= L) return;
 
   const int tid = threadIdx.x;
-  const int wid = tid >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int r = lane & 31;
   const int hh = lane >> 5;
-  const size_t rs = (size_t)p.heads * D;  // row stride in elements
+  const int nh = r >> 4, gi = lane & 15;
+  const int rs = p.heads * D;  // row stride in elements (< 2^31 by the host checks)
   const size_t base = ((size_t)seq_start * p.heads + h) * D;
   const uint16_t* __restrict__ qg = p.q + base;
   const uint16_t* __restrict__ kg = p.k + base;
@@ -99,13 +115,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKernelArgs p) {
   const int myq = qw + r;
   const bool wave_active = qw < L;
 
-  // ---- Q fragments (B operand of S^T = K Q^T): lane holds Q[myq][16*kk + 8*hh .. +7]
+  // ---- Q fragments (B operand of S^T = K Q^T): lane holds Q[myq][16*kk + 8*hh .. +7].
+  // Rows past the end read the last row (finite values, never stored).
   bf16x8 qf[KK];
+  {
+    const uint16_t* qrow = qg + (size_t)min(myq, L - 1) * rs + 8 * hh;
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (myq < L) x = *(const u32x4*)(qg + (size_t)myq * rs + 16 * kk + 8 * hh);
-    qf[kk] = __builtin_bit_cast(bf16x8, x);
+    for (int kk = 0; kk < KK; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * kk));
   }
 
   int ntiles = (L + kBC - 1) / kBC;
@@ -114,34 +130,53 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKernelArgs p) {
     ntiles = min(ntiles, last_q / kBC + 1);
   }
 
-  // ---- staging: thread t moves chunks t, t+NT, ... of each tile (16 lanes per row)
-  u32x4 kreg[LOADS], vreg[LOADS];
-  auto load_tile = [&](int kt) {
+  // ---- staging: wave-load `it` of this wave fills tile rows
+  // lrow = (wid*LOADS + it) * ROWS_PER_KB + lane / CH at physical chunk lane % CH; the lane
+  // fetches the logical chunk that the swizzle puts there. Sources are a uniform tile base
+  // plus a 32-bit per-lane offset (loop invariant except in a ragged last tile, where rows
+  // past the end re-read the last row; they are masked later).
+  auto lane_src = [&](int it, int last_row, int& koff, int& voff) {
+    const int lrow = (wid * LOADS + it) * ROWS_PER_KB + lane / CH;
+    const int phys = lane % CH;
+    const int row = min(lrow, last_row);
+    koff = row * rs + (phys ^ swz_k<D>(lrow)) * 8;
+    voff = row * rs + (phys ^ swz_v<D>(lrow)) * 8;
+  };
+  int k_src[LOADS], v_src[LOADS];
+#pragma unroll
+  for (int it = 0; it < LOADS; ++it) lane_src(it, kBC - 1, k_src[it], v_src[it]);
+  auto issue_tile = [&](int kt, int buf) {
+    const int k0 = kt * kBC;
+    const uint16_t* kt_base = kg + (size_t)k0 * rs;
+    const uint16_t* vt_base = vg + (size_t)k0 * rs;
+    const bool full = k0 + kBC <= L;
 #pragma unroll
     for (int it = 0; it < LOADS; ++it) {
-      const int ci = tid + it * NT;
-      const int row = ci / CH, c = ci % CH;
-      const int key = kt * kBC + row;
-      u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
-      if (key < L) {
-        zk = *(const u32x4*)(kg + (size_t)key * rs + c * 8);
-        zv = *(const u32x4*)(vg + (size_t)key * rs + c * 8);
-      }
-      kreg[it] = zk;
-      vreg[it] = zv;
+      int ko = k_src[it], vo = v_src[it];
+      if (!full) lane_src(it, L - 1 - k0, ko, vo);
+      char* kdst = smem + buf * TILE_B + (wid * LOADS + it) * 1024;
+      char* vdst = smem + (2 + buf) * TILE_B + (wid * LOADS + it) * 1024;
+      copy16_to_lds(kt_base + (unsigned)ko, kdst);
+      copy16_to_lds(vt_base + (unsigned)vo, vdst);
     }
   };
-  auto store_tile = [&](int buf) {
-    uint16_t* ks = smem + buf * TILE;
-    uint16_t* vs = smem + (2 + buf) * TILE;
+
+  // ---- per-lane LDS operand offsets, absolute bytes into smem for buffer 0; the loop
+  // flips bit log2(TILE_B) of every offset to switch buffers (buffer bases are TILE_B aligned).
+  // K (A operand of S^T): row r (+32 for the second half), chunk 2*kk + hh.
+  int k_off[KK];
 #pragma unroll
-    for (int it = 0; it < LOADS; ++it) {
-      const int ci = tid + it * NT;
-      const int row = ci / CH, c = ci % CH;
-      *(u32x4*)(ks + row * D + ((c ^ swz_k<D>(row)) << 3)) = kreg[it];
-      *(u32x4*)(vs + row * D + ((c ^ swz_v<D>(row)) << 3)) = vreg[it];
+  for (int kk = 0; kk < KK; ++kk) k_off[kk] = r * D * 2 + (((2 * kk + hh) ^ swz_k<D>(r)) << 4);
+  // V (A operand of O^T, transpose read): rows 16ks + 8t + 4hh + gi/4, columns db*32 + 16nh + 4(gi%4).
+  int v_off[DB];
+  {
+    const int vrow = 4 * hh + (gi >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int col = db * 32 + 16 * nh + 4 * (gi & 3);
+      v_off[db] = 2 * TILE_B + vrow * D * 2 + ((((col >> 3) ^ swz_v<D>(vrow)) << 3) + (col & 7)) * 2;
     }
-  };
+  }
 
   float m_ref = -1e30f;  // pivot (log2 units of scaled score), shared by both wave halves
   float l_part = 0.f;    // this lane's half of the running sum of P (fp32, for the LSE)
@@ -152,54 +187,51 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKernelArgs p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
 
-  load_tile(0);
-  store_tile(0);
+  const float c2 = p.scale_log2;
+
+  issue_tile(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-
   for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < ntiles) load_tile(kt + 1);
+    if (kt + 1 < ntiles) issue_tile(kt + 1, (kt + 1) & 1);
     const int k0 = kt * kBC;
-    const bool need0 = wave_active && (!CAUSAL || k0 <= qw + 31);
-    if (need0) {
-      const bool need1 = !CAUSAL || (k0 + 32 <= qw + 31);
-      const uint16_t* ks = smem + buf * TILE;
-      const uint16_t* vs = smem + (2 + buf) * TILE;
-
+    if (wave_active && (!CAUSAL || k0 <= qw + 31)) {
       // S^T = K Q^T for the two 32-key halves of the block
       f32x16 s0, s1;
 #pragma unroll
       for (int i = 0; i < 16; ++i) { s0[i] = 0.f; s1[i] = 0.f; }
+      // operands read two k-steps ahead of their MFMAs
+      bf16x8 a0[2], a1[2];
+      a0[0] = __builtin_bit_cast(bf16x8, *(const u32x4*)(smem + k_off[0]));
+      a1[0] = __builtin_bit_cast(bf16x8, *(const u32x4*)(smem + k_off[0] + 32 * D * 2));
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const int c = 2 * kk + hh;
-        const int row0 = r, row1 = 32 + r;
-        bf16x8 a0 = __builtin_bit_cast(bf16x8, *(const u32x4*)(ks + row0 * D + ((c ^ swz_k<D>(row0)) << 3)));
-        s0 = mfma32(a0, qf[kk], s0);
-        if (need1) {
-          bf16x8 a1 = __builtin_bit_cast(bf16x8, *(const u32x4*)(ks + row1 * D + ((c ^ swz_k<D>(row1)) << 3)));
-          s1 = mfma32(a1, qf[kk], s1);
+        if (kk + 1 < KK) {
+          a0[(kk + 1) & 1] = __builtin_bit_cast(bf16x8, *(const u32x4*)(smem + k_off[kk + 1]));
+          a1[(kk + 1) & 1] = __builtin_bit_cast(bf16x8, *(const u32x4*)(smem + k_off[kk + 1] + 32 * D * 2));
         }
+        s0 = mfma32(a0[kk & 1], qf[kk], s0);
+        s1 = mfma32(a1[kk & 1], qf[kk], s1);
       }
-
-      // masking: causal diagonal block, ragged tail, skipped half
-      const bool edge = (CAUSAL && k0 + kBC - 1 > qw) || (k0 + kBC > L);
-      if (edge || !need1) {
+      // causal diagonal block or ragged tail: mask (wave-uniform branch)
+      if ((CAUSAL && k0 + kBC - 1 > qw) || (k0 + kBC > L)) {
+        const int lim = CAUSAL ? min(myq, L - 1) : L - 1;  // last visible key of this row
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int kl = 8 * (i >> 2) + 4 * hh + (i & 3);
-          const int key0 = k0 + kl, key1 = k0 + 32 + kl;
-          if ((CAUSAL && key0 > myq) || key0 >= L) s0[i] = -INFINITY;
-          if (!need1 || (CAUSAL && key1 > myq) || key1 >= L) s1[i] = -INFINITY;
+          const int kl = k0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+          s0[i] = kl > lim ? -INFINITY : s0[i];
+          s1[i] = kl + 32 > lim ? -INFINITY : s1[i];
         }
       }
 
-      // online softmax (base 2). Row max over this lane's 32 scores, then the other half.
-      float mx = fmaxf(s0[0], s1[0]);
+      // row max over this lane's 32 scores (raw), then across the two wave halves
+      float ma = max3(s0[0], s0[1], s1[0]), mb = max3(s1[1], s0[2], s1[2]);
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-      mx = pair_max(mx);
-      const float mt = mx * p.scale_log2;
+      for (int i = 3; i < 16; i += 2) {
+        ma = max3(ma, s0[i], s1[i]);
+        if (i + 1 < 16) mb = max3(mb, s0[i + 1], s1[i + 1]);
+      }
+      const float mt = pair_max(fmaxf(ma, mb)) * c2;
       if (wave_any(mt > m_ref + kRescaleThreshold)) {
         const float m_new = fmaxf(m_ref, mt);
         const float alpha = exp2_fast(m_ref - m_new);
@@ -211,21 +243,26 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKernelArgs p) {
           for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
         m_ref = m_new;
       }
-      float ls = 0.f;
+      const float mneg = -m_ref;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        s0[i] = exp2_fast(__builtin_fmaf(s0[i], p.scale_log2, -m_ref));
-        s1[i] = exp2_fast(__builtin_fmaf(s1[i], p.scale_log2, -m_ref));
-        ls += s0[i] + s1[i];
+        s0[i] = exp2_fast(__builtin_fmaf(s0[i], c2, mneg));
+        s1[i] = exp2_fast(__builtin_fmaf(s1[i], c2, mneg));
       }
-      l_part += ls;
+      // tree sum of the 32 values
+      float t[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) t[i] = s0[i] + s1[i];
+#pragma unroll
+      for (int n = 8; n >= 1; n >>= 1)
+#pragma unroll
+        for (int i = 0; i < n; ++i) t[i] += t[i + n];
+      l_part += t[0];
 
-      // O^T += V^T P^T. k-step ks covers block keys 16ks..16ks+15; its B operand is
-      // P^T from score half ks/2, registers 8*(ks%2)..+7 (keys 16ks + 8(e/4) + 4hh + e%4).
-      const int nh = r >> 4, gi = lane & 15;
+      // O^T += V^T P^T. k-step ks covers block keys 16ks..16ks+15; its B operand is P^T from
+      // score half ks/2, registers 8*(ks%2)..+7 (keys 16ks + 8(e/4) + 4hh + e%4).
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        if (ks >= 2 && !need1) break;
         const f32x16& sp = (ks < 2) ? s0 : s1;
         const int o8 = 8 * (ks & 1);
         float pv[8];
@@ -234,45 +271,45 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKernelArgs p) {
         const bf16x8 pb = pack_bf16x8_sum(pv, lr_part);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int col = db * 32 + 16 * nh + 4 * (gi & 3);
-          const int row_a = 16 * ks + 4 * hh + (gi >> 2);
-          const int row_b = row_a + 8;
-          const i16x4 lo = lds_read_tr(vs + row_a * D + (((col >> 3) ^ swz_v<D>(row_a)) << 3) + (col & 7));
-          const i16x4 hi = lds_read_tr(vs + row_b * D + (((col >> 3) ^ swz_v<D>(row_b)) << 3) + (col & 7));
+          const char* va = smem + v_off[db] + 16 * ks * D * 2;
+          const i16x4 lo = lds_read_tr((const uint16_t*)va);
+          const i16x4 hi = lds_read_tr((const uint16_t*)(va + 8 * D * 2));
           oacc[db] = mfma32(join_tr(lo, hi), pb, oacc[db]);
         }
       }
     }
-    if (kt + 1 < ntiles) store_tile(buf ^ 1);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) k_off[kk] ^= TILE_B;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) v_off[db] ^= TILE_B;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile have landed
     __syncthreads();
   }
 
-  // ---- epilogue: one division by l, single bf16 rounding, natural-log LSE
-  if (!wave_active) return;
+  // ---- epilogue: one division, single bf16 rounding, natural-log LSE.
   // O is normalised by the sum of the weights it was accumulated with (bf16-rounded P), so
   // the output is an exact convex combination of the rounded weights; the LSE uses the
   // unrounded sum.
+  if (!wave_active || myq >= L) return;
   const float l_tot = pair_sum(l_part);
   const float lr_tot = pair_sum(lr_part);
   const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
-  if (myq < L) {
-    uint16_t* og = p.o + base + (size_t)myq * rs;
+  uint16_t* og = p.o + base + (size_t)myq * rs;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u32x2 wv;
-        wv[0] = pack_bf16x2(oacc[db][4 * i + 0] * inv, oacc[db][4 * i + 1] * inv);
-        wv[1] = pack_bf16x2(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv);
-        *(u32x2*)(og + db * 32 + 8 * i + 4 * hh) = wv;
-      }
-    if (hh == 0) {
-      const float lse = l_tot > 0.f ? (m_ref + log2_fast(l_tot)) * kLn2 : -INFINITY;
-      if constexpr (VARLEN)
-        p.lse[(size_t)h * p.total_rows + seq_start + myq] = lse;
-      else
-        p.lse[((size_t)bs * p.heads + h) * p.seqlen + myq] = lse;
+    for (int i = 0; i < 4; ++i) {
+      u32x2 wv;
+      wv[0] = pack_bf16x2(oacc[db][4 * i + 0] * inv, oacc[db][4 * i + 1] * inv);
+      wv[1] = pack_bf16x2(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv);
+      *(u32x2*)(og + db * 32 + 8 * i + 4 * hh) = wv;
     }
+  if (hh == 0) {
+    const float lse = l_tot > 0.f ? (m_ref + log2_fast(l_tot)) * kLn2 : -INFINITY;
+    if constexpr (VARLEN)
+      p.lse[(size_t)h * p.total_rows + seq_start + myq] = lse;
+    else
+      p.lse[((size_t)bs * p.heads + h) * p.seqlen + myq] = lse;
   }
 }
 
