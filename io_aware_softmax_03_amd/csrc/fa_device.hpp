@@ -78,6 +78,18 @@ __device__ __forceinline__ bf16x8 pack_bf16x8_sum(const float* a, float& sum) {
                                  __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// acc + the sum of the eight bf16 values (v_dot2_f32_bf16 of each pair against (1, 1)).
+// The pairs are taken with shufflevector: extracting them through an integer bitcast of the
+// vector has been seen to make the compiler feed the same register to every dot2.
+__device__ __forceinline__ float sum_bf16x8(const bf16x8& x, float acc) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), ones, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), ones, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), ones, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), ones, acc, false);
+  return acc;
+}
+
 __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3,
                                               float a4, float a5, float a6, float a7) {
   const bf16x2 p0 = cvt_bf16x2(a0, a1), p1 = cvt_bf16x2(a2, a3);
