@@ -175,8 +175,9 @@ def extra_measurements(steps):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the default warm-up (about a second of launches) lets the GPU clock settle before timing
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=1500)
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -237,7 +238,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profile(),
-                     "kernel": "fwd_bf16_kernel<128, 4, causal>", "launch_ms": round(kern_ms, 4)},
+                     "kernel": "fwd_bf16_kernel<128, causal, dense>", "launch_ms": round(kern_ms, 4)},
         "device": {"name": prop.name, "gcn_arch": getattr(prop, "gcnArchName", ""),
                    "cus": prop.multi_processor_count},
     }

@@ -28,13 +28,22 @@ FLAGS = [
 ]
 
 
+# Per-file extra flags. The forward kernel runs one wave per SIMD with 512 registers; by
+# default the compiler then gives every MFMA the AGPR accumulator form, which would put the
+# score tiles in AGPRs and cost a copy to VGPRs for each softmax step. With the VGPR form the
+# output accumulators and scores sit in VGPRs and the Q operands in AGPRs.
+FILE_FLAGS = {
+    "fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{res.stderr}")

@@ -14,7 +14,13 @@ constexpr int kMaxSplits = 1024;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
-bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
+// Checked on the bit pattern: this file is built with NaNs assumed absent, which lets the
+// compiler drop floating-point NaN tests.
+bool scale_ok(float s) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, s);
+  const uint32_t exp_bits = (b >> 23) & 0xffu;
+  return (b >> 31) == 0u && exp_bits != 0xffu && (b & 0x7fffffffu) != 0u;  // positive, finite, non-zero
+}
 
 int fits(long long a, long long b, long long c, long long d) {
   // a*b*c*d <= kMaxElems for non-negative factors

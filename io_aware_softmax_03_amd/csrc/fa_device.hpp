@@ -31,8 +31,21 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Workgroup and work-item ids read from the hardware registers. The HIP built-in index
+// variables go through device-library functions built with packed fp32 enabled; with that
+// feature switched off for this code they are not inlined but called, and their results lose
+// the compiler's knowledge that they are the same in every lane of a wave.
+__device__ __forceinline__ int group_id_x() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+__device__ __forceinline__ int thread_id_x() { return (int)__builtin_amdgcn_workitem_id_x(); }
+
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// v_mfma_f32_16x16x32_bf16: A (16 x 32): lane holds A[l%16][8*(l/16) .. +7]; B (32 x 16):
+// lane holds B[8*(l/16) .. +7][l%16]; C (16 x 16): lane holds C[4*(l/16) + i][l%16] at acc[i].
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

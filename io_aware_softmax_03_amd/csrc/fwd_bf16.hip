@@ -3,36 +3,38 @@
 // Method ("FlashAttention: IO-aware exact attention", "Tile decomposition" and "Online
 // softmax"; "FlashAttention-2 and -3", "Fewer non-matmul FLOPs", "Parallelism over the
 // sequence", "Split the queries, not the keys"):
-//   * one workgroup per (query block of BR rows, batch*head); the query block stays in
-//     registers while 64-key blocks of K and V stream through LDS (double buffered);
-//   * each wave owns 32 whole query rows, so the running max, running sum and output
-//     accumulator of a row never leave the wave;
-//   * scores are computed transposed, S^T = K Q^T, so the 32 keys x 32 queries MFMA
-//     output leaves one query per lane (16 scores, the other 16 in the lane 32 away) and
-//     the row max / row sum are in-lane plus one swap between wave halves;
-//   * O^T += V^T P^T on MFMA, with P^T taken straight from the score registers and V^T
-//     read from the row-major V tile with the LDS transpose read;
+//   * one workgroup of four waves per (query block of 256 rows, batch*head); the query block
+//     stays in registers while 32-key blocks of K and V stream through LDS (double buffered);
+//   * each wave owns 64 whole query rows (two groups of 32), so the running max, running sum
+//     and output accumulator of a row never leave the wave, and every K or V operand read
+//     from LDS feeds two MFMAs (one per query group);
+//   * scores are computed transposed, S^T = K Q^T, so the 32 keys x 32 queries MFMA output
+//     leaves one query per lane (16 scores, the other 16 in the lane 32 away) and the row
+//     max / row sum are in-lane plus one swap between wave halves;
+//   * O^T += V^T P^T on MFMA, with P^T taken straight from the score registers and V^T read
+//     from the row-major V tile with the LDS transpose read;
 //   * online softmax in base 2 on scaled scores; the pivot is only moved when a block's
 //     maximum exceeds it by more than kRescaleThreshold (exact for any shared pivot,
 //     "And on Blackwell"), so most blocks skip the accumulator rescale;
-//   * key blocks entirely above the causal diagonal are never loaded; within a block, a
-//     wave skips 32-key halves its rows cannot see.
-// gfx950 specifics: K and V tiles go from global memory straight into LDS
-// (global_load_lds_dwordx4, lane i -> bytes 16i of a wave's 1 KB slice), each lane picking
-// the source chunk that lands it at its swizzled position. Within a wave the loop is software
-// pipelined: the MFMAs of the next block's scores run beside the exponentials of this one,
-// and this block's P V MFMAs beside the next block's row maximum.
+//   * key blocks entirely above the causal diagonal are never loaded, and a wave stops at the
+//     last key block its rows can see.
+// gfx950 specifics: one wave per SIMD (512 registers: the output accumulators sit in AGPRs);
+// K and V tiles go from global memory straight into LDS (global_load_lds_dwordx4, lane i ->
+// bytes 16i of a wave's 1 KB slice), each lane picking the source chunk that lands it at its
+// swizzled position. Within a wave the loop is a three-stage software pipeline: while the
+// MFMAs of the next block's scores and of the previous block's P V run, the VALU turns this
+// block's scores into probabilities.
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
 namespace fa {
 namespace {
 
-constexpr int kBC = 64;                    // keys per streamed block
-// instruction classes for __builtin_amdgcn_sched_group_barrier
-constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedVmem = 0x010, kSchedDsRead = 0x100;
+constexpr int kBC = 32;  // keys per streamed block
+constexpr int kNW = 4;   // waves per workgroup
+constexpr int kQW = 64;  // query rows per wave
+constexpr int kBR = kNW * kQW;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: P stays <= 256
-
 
 struct FwdKernelArgs {
   const uint16_t* q;
@@ -45,6 +47,7 @@ struct FwdKernelArgs {
   int seqlen;      // dense sequence length (unused for packed)
   int total_rows;  // LSE row stride for packed, N for dense
   int nqb;         // workgroups per (sequence, head): query blocks, or pairs of them if causal
+  int grid;        // workgroups launched
   float scale_log2;
 };
 
@@ -62,27 +65,53 @@ __device__ __forceinline__ int swz_v(int row) {
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glob_void;
 
-// One wave-wide global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane i's
-// bytes land at lds_wave_base + 16*i. The source is a uniform tile base plus a per-lane
-// 32-bit element offset.
-__device__ __forceinline__ void copy16_to_lds(const uint16_t* tile_base, unsigned elem_off, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((glob_void*)(tile_base + elem_off), (lds_void*)lds_wave_base, 16, 0, 0);
+// One wave-wide copy of 16 bytes per lane from a buffer into LDS (buffer_load_dwordx4 with
+// the LDS destination): lane i's bytes land at lds_wave_base + 16*i. The lane reads at byte
+// offset `off` of the buffer; offsets at or past the buffer's size read as zero.
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t src, unsigned off, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)lds_wave_base, 16, off, 0, 0, 0);
+}
+
+// Buffer resource over `bytes` bytes at `base` (raw addressing, no stride).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
-template <int D, int NW, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKernelArgs p) {
-  constexpr int BR = 32 * NW;
-  constexpr int CH = D / 8;                 // 16-byte chunks per row
-  constexpr int KK = D / 16;                // MFMA k-steps over the head dim
-  constexpr int DB = D / 32;                // 32-wide output blocks over the head dim
-  constexpr int TILE_B = kBC * D * 2;       // bytes of one K or V tile
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>());
+    static_for<B + 1, E>(f);
+  }
+}
+
+// x * alpha, element-wise, rounded back to bf16
+__device__ __forceinline__ bf16x8 scale_bf16x8(const bf16x8& x, float alpha) {
+  const u32x4 w = __builtin_bit_cast(u32x4, x);
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_lo(w[i]) * alpha;
+    f[2 * i + 1] = bf16_hi(w[i]) * alpha;
+  }
+  return pack_bf16x8(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
+}
+
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) {
+  constexpr int KK = D / 16;                 // MFMA k-steps over the head dim
+  constexpr int DB = D / 32;                 // 32-wide output blocks over the head dim
+  constexpr int KS = kBC / 16;               // MFMA k-steps over a key block
+  constexpr int CH = D / 8;                  // 16-byte chunks per row
+  constexpr int TILE_B = kBC * D * 2;        // bytes of one K or V tile
   constexpr int ROWS_PER_KB = 1024 / (2 * D);
-  constexpr int LOADS = TILE_B / 1024 / NW; // 1 KB wave-loads per tile per wave
-  static_assert(TILE_B % (1024 * NW) == 0, "tile must split evenly over waves");
+  constexpr int LOADS = TILE_B / 1024 / kNW; // 1 KB wave-loads per tile per wave
+  static_assert(TILE_B % (1024 * kNW) == 0, "tile must split evenly over waves");
+  static_assert(KS == 2, "the score layout below assumes 32-key blocks");
 
   // Double-buffered K and V tiles, as four separate LDS objects: every access names its
   // buffer at compile time, so the compiler can tell a copy into one buffer from reads of
@@ -91,15 +120,17 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKernelArgs p) {
   __shared__ __attribute__((aligned(1024))) char k_lds1[TILE_B];
   __shared__ __attribute__((aligned(1024))) char v_lds0[TILE_B];
   __shared__ __attribute__((aligned(1024))) char v_lds1[TILE_B];
+  auto kbuf = [&](auto bc) -> char* { return (decltype(bc)::value & 1) ? k_lds1 : k_lds0; };
+  auto vbuf = [&](auto bc) -> char* { return (decltype(bc)::value & 1) ? v_lds1 : v_lds0; };
 
   // ---- work decode: XCD-aware remap (workgroup w runs on XCD w % 8; each XCD gets a
   // contiguous range of (batch*head, block pair)). Causal: workgroup p of a sequence takes
   // query blocks nb-1-p and p (nb blocks in the sequence), so all workgroups do the same
   // number of key blocks; non-causal: one block each.
-  const int total = gridDim.x;
-  const int w = blockIdx.x;
+  const int total = p.grid;
+  const int w = group_id_x();
   const int logical = (total % 8 == 0) ? (w % 8) * (total / 8) + (w / 8) : w;
-  const int pi = logical % p.nqb;  // p.nqb counts work items per (sequence, head)
+  const int pi = logical % p.nqb;
   const int bh = logical / p.nqb;
   const int h = bh % p.heads;
   const int bs = bh / p.heads;
@@ -111,12 +142,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKernelArgs p) {
     seq_start = bs * p.seqlen;
     L = p.seqlen;
   }
-  const int nb = (L + BR - 1) / BR;
+  const int nb = (L + kBR - 1) / kBR;
 
   auto run_block = [&](int qb) {
-    const int q0 = qb * BR;
+    const int q0 = qb * kBR;
 
-    const int tid = threadIdx.x;
+    const int tid = thread_id_x();
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int r = lane & 31;
@@ -128,294 +159,453 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKernelArgs p) {
     const uint16_t* __restrict__ kg = p.k + base;
     const uint16_t* __restrict__ vg = p.v + base;
 
-    const int qw = q0 + 32 * wid;  // first query row of this wave
-    const int myq = qw + r;
+    const int qw = q0 + kQW * wid;  // first query row of this wave
     const bool wave_active = qw < L;
 
-    // ---- Q fragments (B operand of S^T = K Q^T): lane holds Q[myq][16*kk + 8*hh .. +7].
-    // Rows past the end read the last row (finite values, never stored).
-    bf16x8 qf[KK];
-    {
-      const uint16_t* qrow = qg + (size_t)min(myq, L - 1) * rs + 8 * hh;
-  #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * kk));
+    // ---- Q fragments (B operand of S^T = K Q^T): lane holds, for query group g, row
+    // qw + 32g + r, dims 16kk + 8hh .. +7. Rows past the end read the last row (finite
+    // values, never stored).
+    bf16x8 qf[2][KK];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const uint16_t* qrow = qg + (size_t)min(qw + 32 * g + r, L - 1) * rs + 8 * hh;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) qf[g][kk] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * kk));
     }
+    // the Q operands live in AGPRs (MFMA reads its A and B operands from either file), leaving
+    // the VGPRs to the scores and probabilities the VALU works on
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+a"(qf[g][kk]));
 
     int ntiles = (L + kBC - 1) / kBC;
-    if constexpr (CAUSAL) {
-      const int last_q = min(q0 + BR, L) - 1;
-      ntiles = min(ntiles, last_q / kBC + 1);
-    }
+    if constexpr (CAUSAL) ntiles = min(ntiles, (min(q0 + kBR, L) - 1) / kBC + 1);
+    // key blocks this wave computes (causal: those with a key its rows can see); every wave
+    // takes part in all of the block's loads and barriers
+    int wtiles = 0;
+    if (wave_active) wtiles = CAUSAL ? min(ntiles, min(qw + kQW - 1, L - 1) / kBC + 1) : ntiles;
 
     // ---- staging: wave-load `it` of this wave fills tile rows
     // lrow = (wid*LOADS + it) * ROWS_PER_KB + lane / CH at physical chunk lane % CH; the lane
-    // fetches the logical chunk that the swizzle puts there. Sources are a uniform tile base
-    // plus a 32-bit per-lane offset (loop invariant except in a ragged last tile, where rows
-    // past the end re-read the last row; they are masked later).
-    auto lane_src = [&](int it, int last_row, int& koff, int& voff) {
+    // fetches the logical chunk that the swizzle puts there. Each copy goes through a buffer
+    // resource that ends with the sequence, so rows past the end arrive as zeros (masked
+    // later); the per-lane byte offsets are the same for every tile.
+    unsigned k_src[LOADS], v_src[LOADS];
+#pragma unroll
+    for (int it = 0; it < LOADS; ++it) {
       const int lrow = (wid * LOADS + it) * ROWS_PER_KB + lane / CH;
       const int phys = lane % CH;
-      const int row = min(lrow, last_row);
-      koff = row * rs + (phys ^ swz_k<D>(lrow)) * 8;
-      voff = row * rs + (phys ^ swz_v<D>(lrow)) * 8;
-    };
+      k_src[it] = (unsigned)(lrow * rs + (phys ^ swz_k<D>(lrow)) * 8) * 2u;
+      v_src[it] = (unsigned)(lrow * rs + (phys ^ swz_v<D>(lrow)) * 8) * 2u;
+    }
     // copy key block kt of K (IS_K) or V into buffer BUF
     auto issue = [&](auto is_kc, auto bufc, int kt) {
       constexpr bool IS_K = decltype(is_kc)::value;
-      constexpr int BUF = decltype(bufc)::value;
       const int k0 = kt * kBC;
-      const uint16_t* t_base = (IS_K ? kg : vg) + (size_t)k0 * rs;
-      char* dst = (IS_K ? (BUF ? k_lds1 : k_lds0) : (BUF ? v_lds1 : v_lds0)) + wid * LOADS * 1024;
-      const int last_row = min(kBC - 1, L - 1 - k0);
-  #pragma unroll
-      for (int it = 0; it < LOADS; ++it) {
-        int ko, vo;
-        lane_src(it, last_row, ko, vo);
-        copy16_to_lds(t_base, (unsigned)(IS_K ? ko : vo), dst + it * 1024);
-      }
+      const unsigned bytes = (unsigned)(min(kBC - 1, L - 1 - k0) * rs + D) * 2u;
+      const __amdgpu_buffer_rsrc_t src = make_rsrc((IS_K ? kg : vg) + (size_t)k0 * rs, bytes);
+      char* dst = (IS_K ? kbuf(bufc) : vbuf(bufc)) + wid * LOADS * 1024;
+#pragma unroll
+      for (int it = 0; it < LOADS; ++it) copy16_to_lds(src, IS_K ? k_src[it] : v_src[it], dst + it * 1024);
     };
 
     // ---- per-lane LDS operand offsets, bytes within a tile buffer
-    // K (A operand of S^T): row r (+32 for the second half), chunk 2*kk + hh.
+    // K (A operand of S^T): row r, chunk 2*kk + hh.
     int k_off[KK];
-  #pragma unroll
+#pragma unroll
     for (int kk = 0; kk < KK; ++kk) k_off[kk] = r * D * 2 + (((2 * kk + hh) ^ swz_k<D>(r)) << 4);
     // V (A operand of O^T, transpose read): rows 16ks + 8t + 4hh + gi/4, columns db*32 + 16nh + 4(gi%4).
     int v_off[DB];
     {
       const int vrow = 4 * hh + (gi >> 2);
-  #pragma unroll
+#pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int col = db * 32 + 16 * nh + 4 * (gi & 3);
         v_off[db] = vrow * D * 2 + ((((col >> 3) ^ swz_v<D>(vrow)) << 3) + (col & 7)) * 2;
       }
     }
     // keep these per-block values from being hoisted out of the block loop, where they
-    // would stay live across both causal passes and be spilled
+    // would stay live across both causal passes
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(k_off[kk]));
 #pragma unroll
     for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(v_off[db]));
+#pragma unroll
+    for (int it = 0; it < LOADS; ++it) asm volatile("" : "+v"(k_src[it]), "+v"(v_src[it]));
 
-    float m_ref = -1e30f;  // pivot (log2 units of scaled score), shared by both wave halves
-    float l_part = 0.f;    // this lane's half of the running sum of P (fp32, for the LSE)
-    float lr_part = 0.f;   // the same sum over P as rounded to bf16 for the MFMA (normalises O)
-    f32x16 oacc[DB];
-  #pragma unroll
-    for (int db = 0; db < DB; ++db)
-  #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+    // per query group: pivot (log2 units of scaled score, shared by both wave halves), this
+    // lane's half of the running fp32 sum of P (for the LSE), and of the sum of P as rounded
+    // to bf16 for the MFMA (normalises O)
+    float m_ref[2] = {-1e30f, -1e30f};
+    float l_part[2] = {0.f, 0.f};
+    float lr_part[2] = {0.f, 0.f};
+    // Sums of the rounded P formed on the matrix core: v_mfma_f32_16x16x32_bf16 with a 0/1
+    // selector as A and a P^T operand as B. Read as a 16x16x32 B operand, the P^T register of
+    // lane l is column l%16, k-block l/16; blocks 0 and 2 hold query l%16 (both wave halves),
+    // blocks 1 and 3 query l%16 + 16. Selector rows 0-7 take blocks 0 and 2, rows 8-15 blocks
+    // 1 and 3, so every output row is a complete 16-key sum; lane l ends up holding the sum
+    // of query q16(l) = l%16 + 16*(l/32) (four equal copies).
+    f32x4 lsum[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    bf16x8 sel;
+    {
+      const __bf16 one = (((lane >> 4) & 1) == ((lane & 15) >= 8)) ? (__bf16)1.0f : (__bf16)0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sel[e] = one;
+    }
+    const int lane_q16 = (lane & 15) + 16 * (lane >> 5);  // query whose sum lane holds in lsum
+    f32x16 oacc[2][DB];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[g][db][i] = 0.f;
 
     const float c2 = p.scale_log2;
 
-    // Tiles this wave computes (causal: those with a key its rows can see). All waves take
-    // part in every tile's loads and barriers.
-    int wtiles = 0;
-    if (wave_active) wtiles = CAUSAL ? min(ntiles, min(qw + 31, L - 1) / kBC + 1) : ntiles;
-
-    // S^T = K Q^T for one key block from the K buffer the offsets currently point at
-    auto qk = [&](f32x16& s0, f32x16& s1, auto bufc) {
-      const char* kb = decltype(bufc)::value ? k_lds1 : k_lds0;
-  #pragma unroll
-      for (int i = 0; i < 16; ++i) { s0[i] = 0.f; s1[i] = 0.f; }
-      bf16x8 a0[2], a1[2];
-      a0[0] = __builtin_bit_cast(bf16x8, *(const u32x4*)(kb + k_off[0]));
-      a1[0] = __builtin_bit_cast(bf16x8, *(const u32x4*)(kb + k_off[0] + 32 * D * 2));
-  #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        if (kk + 1 < KK) {
-          a0[(kk + 1) & 1] = __builtin_bit_cast(bf16x8, *(const u32x4*)(kb + k_off[kk + 1]));
-          a1[(kk + 1) & 1] = __builtin_bit_cast(bf16x8, *(const u32x4*)(kb + k_off[kk + 1] + 32 * D * 2));
-        }
-        s0 = mfma32(a0[kk & 1], qf[kk], s0);
-        s1 = mfma32(a1[kk & 1], qf[kk], s1);
-      }
-    };
-    // mask a causal-diagonal or ragged block (wave-uniform test)
-    auto mask = [&](f32x16& s0, f32x16& s1, int k0) {
-      if ((CAUSAL && k0 + kBC - 1 > qw) || (k0 + kBC > L)) {
-        const int lim = CAUSAL ? min(myq, L - 1) : L - 1;  // last visible key of this row
-  #pragma unroll
+    // score s[g][i] of a block is S^T[key k0 + 8(i/4) + 4hh + i%4][query qw + 32g + r]
+    auto edge = [&](int k0) { return (CAUSAL && k0 + kBC - 1 > qw) || (k0 + kBC > L); };
+    auto mask = [&](f32x16 (&s)[2], int k0) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int lim = CAUSAL ? min(qw + 32 * g + r, L - 1) : L - 1;  // last visible key
+#pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int kl = k0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          s0[i] = kl > lim ? -INFINITY : s0[i];
-          s1[i] = kl + 32 > lim ? -INFINITY : s1[i];
+          s[g][i] = kl > lim ? -INFINITY : s[g][i];
         }
       }
     };
-    // the block's row maximum (log2 units), over this lane's 32 scores and the other half's
-    auto rowmax = [&](const f32x16& s0, const f32x16& s1) {
-      float ma = max3(s0[0], s0[1], s1[0]), mb = max3(s1[1], s0[2], s1[2]);
-  #pragma unroll
-      for (int i = 3; i < 16; i += 2) {
-        ma = max3(ma, s0[i], s1[i]);
-        if (i + 1 < 16) mb = max3(mb, s0[i + 1], s1[i + 1]);
-      }
+    // block row maximum of query group g (log2 units), over both wave halves
+    auto rowmax = [&](const f32x16& s) {
+      float ma = max3(s[0], s[1], s[2]), mb = max3(s[3], s[4], s[5]);
+      ma = max3(ma, s[6], s[7]);
+      mb = max3(mb, s[8], s[9]);
+      ma = max3(ma, s[10], s[11]);
+      mb = max3(mb, s[12], s[13]);
+      ma = max3(ma, s[14], s[15]);
       return pair_max(fmaxf(ma, mb)) * c2;
     };
-    // move the pivot when the block maximum exceeds it by more than the threshold (rare),
-    // rescaling O and both sums to the new pivot
-    auto repivot = [&](bool apply, float mt) {
-      if (wave_any(apply && mt > m_ref + kRescaleThreshold)) {
-        const float m_new = apply ? fmaxf(m_ref, mt) : m_ref;
-        const float alpha = exp2_fast(m_ref - m_new);
-        l_part *= alpha;
-        lr_part *= alpha;
-  #pragma unroll
-        for (int db = 0; db < DB; ++db)
-  #pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-        m_ref = m_new;
-      }
-    };
-    // P = exp2(S*c - pivot), in place, and as four bf16x8 MFMA operands (k-step ks holds
-    // score half ks/2, registers 8*(ks%2)..+7, i.e. keys 16ks + 8(e/4) + 4hh + e%4)
-    auto exp_pack = [&](f32x16& s0, f32x16& s1, bf16x8* pb) {
-      const float mneg = -m_ref;
-      float la = 0.f, lb = 0.f;  // fp32 sum of P (for the LSE), two chains
-  #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s0[i] = exp2_fast(__builtin_fmaf(s0[i], c2, mneg));
-        s1[i] = exp2_fast(__builtin_fmaf(s1[i], c2, mneg));
-        la += s0[i];
-        lb += s1[i];
-      }
-      l_part += la + lb;
-  #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const f32x16& sp = (ks < 2) ? s0 : s1;
-        const int o = 8 * (ks & 1);
-        pb[ks] = pack_bf16x8(sp[o], sp[o + 1], sp[o + 2], sp[o + 3], sp[o + 4], sp[o + 5], sp[o + 6], sp[o + 7]);
-      }
-    };
-    // running sum of the bf16-rounded P the MFMA used (normalises O)
-    auto sums = [&](const bf16x8* pb) {
-  #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) lr_part = sum_bf16x8(pb[ks], lr_part);
-    };
-    // O^T += V^T P^T from the V buffer the offsets currently point at
-    auto pv = [&](const bf16x8* pb, auto bufc) {
-      const char* vb = decltype(bufc)::value ? v_lds1 : v_lds0;
-  #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-  #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const char* va = vb + v_off[db] + 16 * ks * D * 2;
-          const i16x4 lo = lds_read_tr((const uint16_t*)va);
-          const i16x4 hi = lds_read_tr((const uint16_t*)(va + 8 * D * 2));
-          oacc[db] = mfma32(join_tr(lo, hi), pb[ks], oacc[db]);
+    // Move a group's pivot when the block maximum exceeds it by more than the threshold
+    // (rare), rescaling O, both sums and the P block not yet multiplied into O.
+    auto repivot = [&](const float (&mt)[2], bf16x8 (&pend)[2][KS]) {
+      const bool up = mt[0] > m_ref[0] + kRescaleThreshold || mt[1] > m_ref[1] + kRescaleThreshold;
+      if (wave_any(up)) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const float m_new = fmaxf(m_ref[g], mt[g]);
+          const float alpha = exp2_fast(m_ref[g] - m_new);
+          l_part[g] *= alpha;
+          lr_part[g] *= alpha;
+          lsum[g] *= __int_as_float(__builtin_amdgcn_ds_bpermute(4 * lane_q16, __float_as_int(alpha)));
+          // one 16-register block at a time (the accumulators are in AGPRs: each value goes
+          // through a VGPR), so this rare path does not raise the kernel's register count
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[g][db][i] *= alpha;
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) pend[g][ks] = scale_bf16x8(pend[g][ks], alpha);
+          m_ref[g] = m_new;
         }
+      }
     };
-    // Software pipeline, per wave: iteration j computes P(j) (VALU) while the MFMAs of
-    // S(j+1) = K(j+1) Q^T run, then O += V(j) P(j) (MFMA) while S(j+1) is masked and its
-    // maximum folded into the pivot (VALU). K is loaded one block ahead of V: during
-    // iteration j the loads of K(j+2) and V(j+1) go to the buffers K(j) and V(j-1) left.
+    // running sums of the bf16-rounded P the MFMA uses
+    auto rsums = [&](const bf16x8 (&pb)[2][KS]) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) lr_part[g] = sum_bf16x8(pb[g][ks], lr_part[g]);
+    };
+    // S^T = K Q^T for both query groups from K buffer BUF
+    auto qk = [&](f32x16 (&s)[2], auto bufc) {
+      const char* kb = kbuf(bufc);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(kb + k_off[kk]));
+        if (kk == 0) {
+          s[0] = mfma32(a, qf[0][0], f32x16{});
+          s[1] = mfma32(a, qf[1][0], f32x16{});
+        } else {
+          s[0] = mfma32(a, qf[0][kk], s[0]);
+          s[1] = mfma32(a, qf[1][kk], s[1]);
+        }
+      }
+    };
+    // V^T operand of k-step ks, output block db, from V buffer BUF
+    auto vread = [&](auto bufc, int ks, int db) {
+      const char* va = vbuf(bufc) + v_off[db] + 16 * ks * D * 2;
+      return join_tr(lds_read_tr((const uint16_t*)va), lds_read_tr((const uint16_t*)(va + 8 * D * 2)));
+    };
+    // O^T += V^T P^T for k-step ks of both query groups
+    auto pv_step = [&](const bf16x8 (&va)[DB], const bf16x8 (&pb)[2][KS], int ks) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        oacc[0][db] = mfma32(va[db], pb[0][ks], oacc[0][db]);
+        oacc[1][db] = mfma32(va[db], pb[1][ks], oacc[1][db]);
+      }
+    };
+    // the last P block of a wave, multiplied into O on its own
+    auto pv_tail = [&](const bf16x8 (&pb)[2][KS], auto bufc) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8 va[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) va[db] = vread(bufc, ks, db);
+        pv_step(va, pb, ks);
+      }
+      rsums(pb);
+    };
+
+    // Values a pipeline part produces are pinned in VGPRs at its end, so that neither the IR
+    // optimisers (which would sink them past the part, next to their first use) nor the
+    // register allocator (AGPRs) move them out of the part they are scheduled in.
+    auto pin = [&](bf16x8 (&pb)[KS], float& a, float (&b)[2]) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(pb[ks]));
+      asm volatile("" : "+v"(a), "+v"(b[0]), "+v"(b[1]));
+    };
+
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
     using KT = std::integral_constant<bool, true>;
     using VT = std::integral_constant<bool, false>;
+
+    // ---- prologue: K(0) -> K buffer 0, K(1) -> K buffer 1; V buffer 1 is cleared so the
+    // first step's P V (a zero P block times that buffer) adds exact zeros
     issue(KT(), B0(), 0);
-    issue(VT(), B0(), 0);
-    if (ntiles > 1) issue(KT(), B1(), 1);
+    issue(KT(), B1(), min(1, ntiles - 1));
+    {
+      u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int o = tid * 16; o < TILE_B; o += kNW * 64 * 16) *(u32x4*)(v_lds1 + o) = z;
+    }
+    f32x16 sA[2], sB[2];
+    bf16x8 pA[2][KS], pB[2][KS];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) pB[g][ks] = bf16x8{};
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    f32x16 sA0, sA1, sB0, sB1;
-    auto edge = [&](int k0) { return (CAUSAL && k0 + kBC - 1 > qw) || (k0 + kBC > L); };
     if (wtiles > 0) {
-      qk(sA0, sA1, B0());
-      if (!edge(0)) repivot(true, rowmax(sA0, sA1));
+      qk(sA, B0());
+      asm volatile("" : "+v"(sA[0]), "+v"(sA[1]));
+      if (edge(0)) mask(sA, 0);
+      const float mt[2] = {rowmax(sA[0]), rowmax(sA[1])};
+      repivot(mt, pB);
     }
-    __syncthreads();   // every wave is done with K(0): its buffer takes K(2)
+    __syncthreads();  // every wave is done with K(0)
 
-    auto iteration = [&](auto parity, int j) {
-      constexpr bool ODD = decltype(parity)::value;
-      f32x16& c0 = ODD ? sB0 : sA0;  // S(j)
-      f32x16& c1 = ODD ? sB1 : sA1;
-      f32x16& n0 = ODD ? sA0 : sB0;  // S(j+1)
-      f32x16& n1 = ODD ? sA1 : sB1;
-      // iteration j reads K(j+1) from K buffer !ODD and V(j) from V buffer ODD, and refills
-      // K buffer ODD with K(j+2) and V buffer !ODD with V(j+1)
-      using Pc = std::integral_constant<int, ODD ? 1 : 0>;
-      using Qc = std::integral_constant<int, ODD ? 0 : 1>;
-      // Loads of K(j+2) and V(j+1); past the last block the last block is loaded again (its
-      // buffer is free and the copy is never read), which keeps phase B free of branches.
-      const int kt_next = min(j + 2, ntiles - 1), vt_next = min(j + 1, ntiles - 1);
-      if (j < wtiles) {
-        // a diagonal or ragged block is masked, and its pivot taken, only now
-        if (edge(j * kBC)) {
-          mask(c0, c1, j * kBC);
-          repivot(true, rowmax(c0, c1));
+    // ---- step j (parity PH = j & 1), for j < wtiles: loads K(j+2) -> K buffer j&1 and
+    // V(j) -> V buffer j&1; computes S(j+1) = K(j+1) Q^T from K buffer !(j&1), P(j) from S(j),
+    // and O += V(j-1) P(j-1) from V buffer !(j&1). Past the last block the loads repeat the
+    // last block (its buffer is free and the copy is never read), so a step has no branches.
+    //
+    // The step is laid out by hand as NSLOT slots, one MFMA each (the score MFMAs first, then
+    // those of P V), fenced by scheduling barriers. Each slot also carries a fixed share of
+    // the VALU work on P(j) (scale-and-shift FMA, exponential, fp32 sum, bf16 packing), the
+    // rounded sums of P(j-1), the row maximum of S(j+1) once its MFMAs are done, and LDS
+    // reads a few slots ahead of the MFMA that consumes them.
+    constexpr int NQK = 2 * KK;               // score MFMAs (both query groups)
+    constexpr int NSLOT = NQK + 2 * KS * DB;  // + P V MFMAs
+    constexpr int VPS = 32 / NSLOT;           // probabilities per slot (1 for D=128, 2 for D=64)
+    static_assert(32 % NSLOT == 0, "slot plan");
+    // slot plan (slot -1 is the preamble before the first MFMA, slot NSLOT the tail after the last)
+    auto fma_slot = [](int v) { return v / VPS - 1; };
+    auto exp_slot = [](int v) { return v / VPS; };
+    auto add_slot = [](int v) { return v / VPS + 1 < NSLOT ? v / VPS + 1 : NSLOT; };
+    auto cvt_slot = [](int q) { return (2 * q + 1) / VPS + 1 < NSLOT ? (2 * q + 1) / VPS + 1 : NSLOT; };
+    auto lsum_slot = [](int k) { return 1 + k * (NQK / (2 * KS)); };  // during the score MFMAs
+    auto kread_slot = [](int kk) { return kk < 3 ? -1 : 2 * kk - 4; };
+    auto vread_slot = [](int ks, int db, int hf) {
+      const int t = NQK + 2 * DB * ks + 2 * db - 6 + hf;
+      return t < -1 ? -1 : t;
+    };
+    // row-maximum op k (0..9) of query group g
+    auto rmax_slot = [](int g, int k) {
+      const int base = NQK + 2 + g * ((NSLOT - NQK - 2) / 2);
+      return base + k / 2 < NSLOT ? base + k / 2 : NSLOT;
+    };
+
+    auto step = [&](auto phase, int j) {
+      constexpr int PH = decltype(phase)::value;
+      constexpr bool ODD = PH & 1;
+      f32x16(&c)[2] = ODD ? sB : sA;       // S(j)
+      f32x16(&n)[2] = ODD ? sA : sB;       // S(j+1)
+      bf16x8(&pc)[2][KS] = ODD ? pB : pA;  // P(j)
+      bf16x8(&pp)[2][KS] = ODD ? pA : pB;  // P(j-1)
+      const char* kb = kbuf(std::integral_constant<int, PH + 1>());  // K(j+1)
+      const char* vb = vbuf(std::integral_constant<int, PH + 1>());  // V(j-1)
+      const float mneg[2] = {-m_ref[0], -m_ref[1]};
+      bf16x8 ka[3];
+      i16x4 vlo[KS][DB], vhi[KS][DB];
+      float acc[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      bf16x2 pr[16];  // P(j) pairs: pair q holds values 2q, 2q+1 (value v = 16g + i is c[g][i])
+      float ma[2], mb[2], mt[2];
+
+      auto slot = [&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        // (plain unrolled loops: with t fixed, every condition below folds at compile time)
+        // LDS reads
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+          if (kread_slot(kk) == t) ka[kk % 3] = __builtin_bit_cast(bf16x8, *(const u32x4*)(kb + k_off[kk]));
+#pragma unroll
+        for (int x = 0; x < KS * DB * 2; ++x) {
+          const int ks = x / (2 * DB), db = (x / 2) % DB, hf = x % 2;
+          if (vread_slot(ks, db, hf) == t) {
+            const uint16_t* a = (const uint16_t*)(vb + v_off[db] + 16 * ks * D * 2 + hf * 8 * D * 2);
+            if (hf == 0) vlo[ks][db] = lds_read_tr(a);
+            else vhi[ks][db] = lds_read_tr(a);
+          }
         }
-        // S(j+1) is formed even past this wave's last block (stale LDS, never used) so that
-        // phase A and phase B each stay one basic block the scheduler can interleave
-        const bool more = j + 1 < wtiles && !edge((j + 1) * kBC);
-        bf16x8 pb[4];
-        // phase A: 16 MFMAs of S(j+1) interleaved with the 32 exponentials, 32 FMAs, 32 adds
-        // and 16 conversions of P(j)
-        exp_pack(c0, c1, pb);
-        qk(n0, n1, Qc());
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-  #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedValu, 7, 0);
+        // the slot's MFMA
+        if constexpr (t >= 0 && t < NQK) {
+          constexpr int kk = t / 2, g = t % 2;
+          n[g] = mfma32(ka[kk % 3], qf[g][kk], kk == 0 ? f32x16{} : n[g]);
+        } else if constexpr (t >= NQK && t < NSLOT) {
+          constexpr int u = t - NQK, ks = u / (2 * DB), db = (u / 2) % DB, g = u % 2;
+          oacc[g][db] = mfma32(join_tr(vlo[ks][db], vhi[ks][db]), pp[g][ks], oacc[g][db]);
         }
+        // VALU work on P(j)
+#pragma unroll
+        for (int v = 0; v < 32; ++v) {
+          const int g = v / 16, i = v % 16;
+          if ((fma_slot(v) < -1 ? -1 : fma_slot(v)) == t) c[g][i] = __builtin_fmaf(c[g][i], c2, mneg[g]);
+          if (exp_slot(v) == t) c[g][i] = exp2_fast(c[g][i]);
+          if (add_slot(v) == t) acc[g][i % 4] += c[g][i];
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int g = q / 8, i = 2 * (q % 8);
+          if (cvt_slot(q) == t) {
+            pr[q] = cvt_bf16x2(c[g][i], c[g][i + 1]);
+            asm volatile("" : "+v"(pr[q]));  // keeps the conversion in its slot
+          }
+        }
+        // rounded sums of P(j-1) on the matrix core (one 16x16x32 MFMA per k-step and group)
+#pragma unroll
+        for (int k = 0; k < 2 * KS; ++k)
+          if (lsum_slot(k) == t) lsum[k / KS] = mfma16(sel, pp[k / KS][k % KS], lsum[k / KS]);
+        // row maximum of S(j+1): ten ops per query group
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int k = 0; k < 10; ++k) {
+            if (rmax_slot(g, k) != t) continue;
+            if (k == 0) ma[g] = max3(n[g][0], n[g][1], n[g][2]);
+            if (k == 1) mb[g] = max3(n[g][3], n[g][4], n[g][5]);
+            if (k >= 2 && k <= 6) {
+              if (k % 2 == 0) ma[g] = max3(ma[g], n[g][2 * k + 2], n[g][2 * k + 3]);
+              else mb[g] = max3(mb[g], n[g][2 * k + 2], n[g][2 * k + 3]);
+            }
+            if (k == 7) ma[g] = fmaxf(ma[g], mb[g]);
+            if (k == 8) ma[g] = pair_max(ma[g]);
+            if (k == 9) mt[g] = ma[g] * c2;
+          }
         __builtin_amdgcn_sched_barrier(0);
-        // phase B: 16 MFMAs of O += V(j) P(j) interleaved with the rounded-P sum, the row
-        // maximum of S(j+1) and the copies of the next K and V blocks
-        issue(KT(), Pc(), kt_next);
-        issue(VT(), Qc(), vt_next);
-        pv(pb, Pc());
-        sums(pb);
-        const float mt = rowmax(n0, n1);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
-  #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
-          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
-          if (i % 2 == 0 && i / 2 < 2 * LOADS) __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 1);
-          __builtin_amdgcn_sched_group_barrier(kSchedValu, 5, 1);
+      };
+
+      // preamble: this step's copies into LDS, the first LDS reads, the first FMAs
+      issue(KT(), std::integral_constant<int, PH>(), min(j + 2, ntiles - 1));
+      issue(VT(), std::integral_constant<int, PH>(), j);
+      static_for<-1, NSLOT + 1>(slot);
+      // tail: fold the partial sums, assemble the bf16 operands of P(j)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) l_part[g] += (acc[g][0] + acc[g][1]) + (acc[g][2] + acc[g][3]);
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int q = 8 * g + 4 * ks;
+          pc[g][ks] = __builtin_shufflevector(__builtin_shufflevector(pr[q], pr[q + 1], 0, 1, 2, 3),
+                                              __builtin_shufflevector(pr[q + 2], pr[q + 3], 0, 1, 2, 3),
+                                              0, 1, 2, 3, 4, 5, 6, 7);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        repivot(more, mt);
-      } else {
-        issue(KT(), Pc(), kt_next);
-        issue(VT(), Qc(), vt_next);
+      pin(pc[0], l_part[0], lr_part);
+      asm volatile("" : "+v"(lsum[0]), "+v"(lsum[1]));
+      pin(pc[1], l_part[1], mt);
+      __builtin_amdgcn_sched_barrier(0);
+      if (j + 1 < wtiles) {
+        // a diagonal or ragged block is masked, and its maximum taken, only now
+        if (edge((j + 1) * kBC)) {
+          mask(n, (j + 1) * kBC);
+          mt[0] = rowmax(n[0]);
+          mt[1] = rowmax(n[1]);
+        }
+        repivot(mt, pc);
       }
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of K(j+2), V(j+1) have landed
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of K(j+2), V(j) have landed
       __syncthreads();
     };
-    for (int j = 0; j < ntiles; j += 2) {
-      iteration(std::integral_constant<bool, false>(), j);
-      if (j + 1 < ntiles) iteration(std::integral_constant<bool, true>(), j + 1);
+    // a step of a wave past its last key block: its share of the loads, and the barrier
+    auto idle_step = [&](auto phase, int j) {
+      constexpr int PH = decltype(phase)::value;
+      issue(KT(), std::integral_constant<int, PH>(), min(j + 2, ntiles - 1));
+      issue(VT(), std::integral_constant<int, PH>(), j);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    };
+    using F0 = std::integral_constant<int, 0>;
+    using F1 = std::integral_constant<int, 1>;
+    // Every wave runs ntiles steps (the same barriers); only the first wtiles compute, and
+    // the last P block of the wave is multiplied into O right after them.
+    int j = 0;
+    for (; j + 1 < wtiles; j += 2) {
+      step(F0(), j);
+      step(F1(), j + 1);
     }
+    if (j < wtiles) {
+      step(F0(), j);
+      ++j;
+      pv_tail(pA, B0());  // wtiles odd: P(wtiles-1) is in pA, V(wtiles-1) in buffer 0
+    } else if (wtiles > 0) {
+      pv_tail(pB, B1());  // wtiles even: P(wtiles-1) is in pB, V(wtiles-1) in buffer 1
+    }
+    for (; j < ntiles; ++j) {
+      if (j & 1)
+        idle_step(F1(), j);
+      else
+        idle_step(F0(), j);
+    }
+
+    __builtin_amdgcn_s_waitcnt(0);  // no copy into LDS outlives the block
 
     // ---- epilogue: one division, single bf16 rounding, natural-log LSE.
     // O is normalised by the sum of the weights it was accumulated with (bf16-rounded P), so
     // the output is an exact convex combination of the rounded weights; the LSE uses the
     // unrounded sum.
-    if (wave_active && myq < L) {
-    const float l_tot = pair_sum(l_part);
-    const float lr_tot = pair_sum(lr_part);
-    const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
-    uint16_t* og = p.o + base + (size_t)myq * rs;
-  #pragma unroll
-    for (int db = 0; db < DB; ++db)
-  #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u32x2 wv;
-        wv[0] = pack_bf16x2(oacc[db][4 * i + 0] * inv, oacc[db][4 * i + 1] * inv);
-        wv[1] = pack_bf16x2(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv);
-        *(u32x2*)(og + db * 32 + 8 * i + 4 * hh) = wv;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int myq = qw + 32 * g + r;
+      const float l_tot = pair_sum(l_part[g]);
+      // lane r's query sum sits in lsum of lane r (r < 16) or lane r + 16 (r >= 16)
+      const float lr_mf = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (r < 16 ? r : r + 16), __float_as_int(lsum[g][0])));
+      const float lr_tot = pair_sum(lr_part[g]) + lr_mf;
+      if (wave_active && myq < L) {
+        const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
+        uint16_t* og = p.o + base + (size_t)myq * rs;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            u32x2 wv;
+            wv[0] = pack_bf16x2(oacc[g][db][4 * i + 0] * inv, oacc[g][db][4 * i + 1] * inv);
+            wv[1] = pack_bf16x2(oacc[g][db][4 * i + 2] * inv, oacc[g][db][4 * i + 3] * inv);
+            *(u32x2*)(og + db * 32 + 8 * i + 4 * hh) = wv;
+          }
+        if (hh == 0) {
+          const float lse = l_tot > 0.f ? (m_ref[g] + log2_fast(l_tot)) * kLn2 : -INFINITY;
+          if constexpr (VARLEN)
+            p.lse[(size_t)h * p.total_rows + seq_start + myq] = lse;
+          else
+            p.lse[((size_t)bs * p.heads + h) * p.seqlen + myq] = lse;
+        }
       }
-    if (hh == 0) {
-      const float lse = l_tot > 0.f ? (m_ref + log2_fast(l_tot)) * kLn2 : -INFINITY;
-      if constexpr (VARLEN)
-        p.lse[(size_t)h * p.total_rows + seq_start + myq] = lse;
-      else
-        p.lse[((size_t)bs * p.heads + h) * p.seqlen + myq] = lse;
-    }
     }
   };
 
@@ -428,9 +618,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKernelArgs p) {
   }
 }
 
-template <int D, int NW, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
-  constexpr int BR = 32 * NW;
   FwdKernelArgs p;
   p.q = (const uint16_t*)a.q;
   p.k = (const uint16_t*)a.k;
@@ -441,26 +630,22 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.heads = a.heads;
   p.seqlen = a.seqlen;
   p.total_rows = a.total_rows;
-  const int nqb = (a.seqlen + BR - 1) / BR;
+  const int nqb = (a.seqlen + kBR - 1) / kBR;
   p.nqb = CAUSAL ? (nqb + 1) / 2 : nqb;  // causal workgroups take a pair of query blocks
   p.scale_log2 = a.scale * kLog2e;
   const long long blocks = (long long)p.nqb * a.heads * a.batch;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL, VARLEN>), dim3((unsigned)blocks), dim3(NW * 64), 0,
-                     stream, p);
+  p.grid = (int)blocks;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)blocks), dim3(kNW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
-#ifndef FA_FWD_WAVES
-#define FA_FWD_WAVES 4
-#endif
 template <int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
-  constexpr int NW = FA_FWD_WAVES;
   const bool varlen = a.cu_seqlens != nullptr;
-  if (a.causal) return varlen ? launch_t<D, NW, true, true>(a, stream) : launch_t<D, NW, true, false>(a, stream);
-  return varlen ? launch_t<D, NW, false, true>(a, stream) : launch_t<D, NW, false, false>(a, stream);
+  if (a.causal) return varlen ? launch_t<D, true, true>(a, stream) : launch_t<D, true, false>(a, stream);
+  return varlen ? launch_t<D, false, true>(a, stream) : launch_t<D, false, false>(a, stream);
 }
 
 }  // namespace
