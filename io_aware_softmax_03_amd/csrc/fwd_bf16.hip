@@ -419,7 +419,9 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
     auto exp_slot = [](int v) { return v / VPS; };
     auto add_slot = [](int v) { return v / VPS + 1 < NSLOT ? v / VPS + 1 : NSLOT; };
     auto cvt_slot = [](int q) { return (2 * q + 1) / VPS + 1 < NSLOT ? (2 * q + 1) / VPS + 1 : NSLOT; };
-    auto lsum_slot = [](int k) { return 1 + k * (NQK / (2 * KS)); };  // during the score MFMAs
+    // the row-sum MFMAs need no LDS operand: they fill the matrix pipe at the start of the
+    // step while the first K operands are read
+    auto lsum_slot = [](int k) { return -1 + 0 * k; };
     auto kread_slot = [](int kk) { return kk < 3 ? -1 : 2 * kk - 4; };
     auto vread_slot = [](int ks, int db, int hf) {
       const int t = NQK + 2 * DB * ks + 2 * db - 6 + hf;
@@ -510,10 +512,13 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
         __builtin_amdgcn_sched_barrier(0);
       };
 
-      // preamble: this step's copies into LDS, the first LDS reads, the first FMAs
+      // preamble (slot -1): the first LDS reads, the row-sum MFMAs and the first FMAs; then
+      // this step's copies into LDS (their scalar set-up runs while the reads are in flight)
+      slot(std::integral_constant<int, -1>());
       issue(KT(), std::integral_constant<int, PH>(), min(j + 2, ntiles - 1));
       issue(VT(), std::integral_constant<int, PH>(), j);
-      static_for<-1, NSLOT + 1>(slot);
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<0, NSLOT + 1>(slot);
       // tail: fold the partial sums, assemble the bf16 operands of P(j)
 #pragma unroll
       for (int g = 0; g < 2; ++g) l_part[g] += (acc[g][0] + acc[g][1]) + (acc[g][2] + acc[g][3]);
