@@ -40,7 +40,7 @@ struct PreArgs {
 template <int D>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(PreArgs p) {
   constexpr int CH = D / 8;
-  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long gid = (long long)group_id_x() * 256 + thread_id_x();
   const long long row = gid / CH;  // (b, n, h) row index in [B, N, H] order
   const int sub = (int)(gid % CH);
   float acc = 0.f;
@@ -80,6 +80,7 @@ struct MainArgs {
   float* dk;
   float* dv;
   int heads, seqlen, nkb;
+  int grid;  // workgroups launched
   float scale, scale_log2;
 };
 
@@ -110,8 +111,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
   __shared__ __attribute__((aligned(16))) float s_lse[2][kBQ];
   __shared__ __attribute__((aligned(16))) float s_dlt[2][kBQ];
 
-  const int total = gridDim.x;
-  const int w = blockIdx.x;
+  const int total = p.grid;
+  const int w = group_id_x();
   const int logical = (total % 8 == 0) ? (w % 8) * (total / 8) + (w / 8) : w;
   const int kb = logical % p.nkb;             // causal: low key blocks (most work) first
   const int bh = logical / p.nkb;
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
   const float* lse_g = p.lse + ((size_t)b * p.heads + h) * N;
   const float* dlt_g = p.delta + ((size_t)b * p.heads + h) * N;
 
-  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int tid = thread_id_x(), wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5, nh = r >> 4, gi = lane & 15;
   const int kb0 = kb * kBK;
   const int kw = kb0 + 32 * wid;  // first key of this wave
@@ -369,6 +370,7 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
   m.scale_log2 = a.scale * kLog2e;
   const long long blocks = (long long)m.nkb * a.batch * a.heads;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  m.grid = (int)blocks;
   return a.causal ? launch_main<D, true>(m, (int)blocks, stream) : launch_main<D, false>(m, (int)blocks, stream);
 }
 

@@ -49,12 +49,12 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs p) {
   constexpr int CH = D / 8;             // lanes per key
   constexpr int KPP = kThreads / CH;    // keys per pass over the workgroup
-  const int h = blockIdx.x % p.heads;
-  const int c = (blockIdx.x / p.heads) % p.num_splits;
-  const int b = blockIdx.x / (p.heads * p.num_splits);
+  const int h = group_id_x() % p.heads;
+  const int c = (group_id_x() / p.heads) % p.num_splits;
+  const int b = group_id_x() / (p.heads * p.num_splits);
   const int kbeg = c * p.chunk;
   const int kend = min(kbeg + p.chunk, p.cache_len);
-  const int tid = threadIdx.x;
+  const int tid = thread_id_x();
   const int sub = tid % CH, grp = tid / CH;
 
   float qv[8];
@@ -160,8 +160,8 @@ struct CombineArgs {
 
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(CombineArgs p) {
-  const size_t bh = blockIdx.x;
-  const int d = threadIdx.x;
+  const size_t bh = group_id_x();
+  const int d = thread_id_x();
   const float* pm = p.part_m + bh * p.num_splits;
   const float* pl = p.part_l + bh * p.num_splits;
   const float* po = p.part_o + bh * p.num_splits * D;

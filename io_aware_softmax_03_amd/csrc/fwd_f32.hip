@@ -32,8 +32,8 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args p) {
   __shared__ __attribute__((aligned(16))) float ks[kKT * D];
   __shared__ __attribute__((aligned(16))) float vs[kKT * D];
 
-  const int qb = p.nqb - 1 - (int)(blockIdx.x % p.nqb);
-  const int bh = blockIdx.x / p.nqb;
+  const int qb = p.nqb - 1 - (int)(group_id_x() % p.nqb);
+  const int bh = group_id_x() / p.nqb;
   const int h = bh % p.heads, bs = bh / p.heads;
   int seq_start, L;
   if constexpr (VARLEN) {
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args p) {
   if (q0 >= L) return;
   const size_t rs = (size_t)p.heads * D;
   const size_t base = ((size_t)seq_start * p.heads + h) * D;
-  const int tid = threadIdx.x;
+  const int tid = thread_id_x();
   const int part = tid % TPR;
   const int myq = q0 + tid / TPR;
   const bool valid = myq < L;
