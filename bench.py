@@ -60,7 +60,28 @@ def time_launches(fn, steps, warmup):
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     ev = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    time_launches.last_median = sorted(ev)[len(ev) // 2]
     return wall_ms, sum(ev) / len(ev), min(ev)
+
+
+def clocks_under_load(fn, launches=400):
+    """GPU clock levels read with rocm-smi while `launches` more calls (untimed) run."""
+    import subprocess
+    import torch
+    for _ in range(launches):
+        fn()
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20).stdout
+    except (OSError, subprocess.SubprocessError):
+        out = ""
+    torch.cuda.synchronize()
+    res = {}
+    for line in out.splitlines():
+        low = line.lower()
+        for key in ("sclk", "mclk", "fclk"):
+            if key + " clock level" in low and "(" in line:
+                res[key + "_mhz"] = line.rsplit("(", 1)[1].split(")")[0].lower().replace("mhz", "").strip()
+    return res
 
 
 def traffic_from_profile():
@@ -212,6 +233,8 @@ def main():
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     step = lambda: fa.fwd(q, k, v, causal=True, out=(o, lse))  # noqa: E731
     wall_ms, kern_ms, kern_min = time_launches(step, args.steps, args.warmup)
+    kern_median = time_launches.last_median
+    clocks = clocks_under_load(step)
     flops = costs.fwd_flops(B, H, N, d, True)
     value = flops / (wall_ms * 1e-3) / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
@@ -238,9 +261,10 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profile(),
-                     "kernel": "fwd_bf16_kernel<128, causal, dense>", "launch_ms": round(kern_ms, 4)},
+                     "kernel": "fwd_bf16_kernel<128, causal, dense>", "launch_ms": round(kern_ms, 4),
+                     "launch_ms_median": round(kern_median, 4), "launch_ms_min": round(kern_min, 4)},
         "device": {"name": prop.name, "gcn_arch": getattr(prop, "gcnArchName", ""),
-                   "cus": prop.multi_processor_count},
+                   "cus": prop.multi_processor_count, "clocks_during_headline": clocks},
     }
     del q, k, v, o, lse
     torch.cuda.empty_cache()

@@ -3,8 +3,9 @@
 // The exact-precision path: same tiled online softmax as the bf16 kernel ("Tile
 // decomposition", "Online softmax"), but the products use fp32 FMAs rather than reduced
 // precision matrix cores, so results stay within fp32 rounding of the exact value.
-// Each query row is owned by D/32 consecutive lanes (32 head dims each); K and V blocks of
-// 32 keys are staged in LDS and read as broadcasts.
+// Each query row is owned by 8 consecutive lanes (D/8 head dims each), so a dot product is
+// a short per-lane FMA chain plus a three-step butterfly; K and V blocks of 32 keys are
+// staged in LDS.
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -27,7 +28,8 @@ struct F32Args {
 
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args p) {
-  constexpr int TPR = D / 32;            // lanes per query row
+  constexpr int TPR = 8;                 // lanes per query row
+  constexpr int DPL = D / TPR;           // head dims per lane
   constexpr int RPB = kThreads / TPR;    // query rows per workgroup
   __shared__ __attribute__((aligned(16))) float ks[kKT * D];
   __shared__ __attribute__((aligned(16))) float vs[kKT * D];
@@ -52,10 +54,10 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args p) {
   const int myq = q0 + tid / TPR;
   const bool valid = myq < L;
 
-  float qv[32], ov[32];
+  float qv[DPL], ov[DPL];
 #pragma unroll
-  for (int c = 0; c < 32; ++c) {
-    qv[c] = valid ? p.q[base + (size_t)myq * rs + part * 32 + c] : 0.f;
+  for (int c = 0; c < DPL; ++c) {
+    qv[c] = valid ? p.q[base + (size_t)myq * rs + part * DPL + c] : 0.f;
     ov[c] = 0.f;
   }
   float m = -1e30f, l = 0.f;
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args p) {
     for (int j = 0; j < kKT; ++j) {
       float acc = 0.f;
 #pragma unroll
-      for (int c = 0; c < 32; ++c) acc = __builtin_fmaf(qv[c], ks[j * D + part * 32 + c], acc);
+      for (int c = 0; c < DPL; ++c) acc = __builtin_fmaf(qv[c], ks[j * D + part * DPL + c], acc);
 #pragma unroll
       for (int off = 1; off < TPR; off <<= 1) acc += __shfl_xor(acc, off);
       const int key = k0 + j;
@@ -96,10 +98,10 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args p) {
     }
     l = l * alpha + ls;
 #pragma unroll
-    for (int c = 0; c < 32; ++c) {
+    for (int c = 0; c < DPL; ++c) {
       float acc = ov[c] * alpha;
 #pragma unroll
-      for (int j = 0; j < kKT; ++j) acc = __builtin_fmaf(s[j], vs[j * D + part * 32 + c], acc);
+      for (int j = 0; j < kKT; ++j) acc = __builtin_fmaf(s[j], vs[j * D + part * DPL + c], acc);
       ov[c] = acc;
     }
     m = m_new;
@@ -107,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args p) {
   if (!valid) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-  for (int c = 0; c < 32; ++c) p.o[base + (size_t)myq * rs + part * 32 + c] = ov[c] * inv;
+  for (int c = 0; c < DPL; ++c) p.o[base + (size_t)myq * rs + part * DPL + c] = ov[c] * inv;
   if (part == 0) {
     const float lse = l > 0.f ? (m + log2_fast(l)) * kLn2 : -INFINITY;
     if constexpr (VARLEN)
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args p) {
 
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
-  constexpr int RPB = kThreads / (D / 32);
+  constexpr int RPB = kThreads / 8;
   F32Args p;
   p.q = (const float*)a.q;
   p.k = (const float*)a.k;
