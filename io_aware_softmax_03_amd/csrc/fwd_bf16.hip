@@ -123,17 +123,28 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
   auto kbuf = [&](auto bc) -> char* { return (decltype(bc)::value & 1) ? k_lds1 : k_lds0; };
   auto vbuf = [&](auto bc) -> char* { return (decltype(bc)::value & 1) ? v_lds1 : v_lds0; };
 
-  // ---- work decode: XCD-aware remap (workgroup w runs on XCD w % 8; each XCD gets a
-  // contiguous range of (batch*head, block pair)). Causal: workgroup p of a sequence takes
-  // query blocks nb-1-p and p (nb blocks in the sequence), so all workgroups do the same
-  // number of key blocks; non-causal: one block each.
+  // ---- work decode, XCD-aware: workgroup w runs on XCD w % 8. With a head count divisible by
+  // 8, XCD x takes heads x, x+8, ... of every sequence (all query blocks of a head share that
+  // XCD's L2 for K and V, and every XCD gets the same mix of sequence lengths); otherwise each
+  // XCD takes a contiguous range of (sequence*head, block). Causal: workgroup p of a sequence
+  // takes query blocks nb-1-p and p (nb blocks in the sequence), so all workgroups of a
+  // sequence do the same number of key blocks; non-causal: one block each.
   const int total = p.grid;
   const int w = group_id_x();
-  const int logical = (total % 8 == 0) ? (w % 8) * (total / 8) + (w / 8) : w;
-  const int pi = logical % p.nqb;
-  const int bh = logical / p.nqb;
-  const int h = bh % p.heads;
-  const int bs = bh / p.heads;
+  int pi, h, bs;
+  if (p.heads % 8 == 0) {
+    const int slot = w / 8, hx = p.heads / 8;
+    pi = slot % p.nqb;
+    const int rest = slot / p.nqb;
+    h = w % 8 + 8 * (rest % hx);
+    bs = rest / hx;
+  } else {
+    const int logical = (total % 8 == 0) ? (w % 8) * (total / 8) + (w / 8) : w;
+    pi = logical % p.nqb;
+    const int bh = logical / p.nqb;
+    h = bh % p.heads;
+    bs = bh / p.heads;
+  }
   int seq_start, L;
   if constexpr (VARLEN) {
     seq_start = p.cu_seqlens[bs];

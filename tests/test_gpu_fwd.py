@@ -55,6 +55,10 @@ def test_fwd_f32(B, N, H, d, causal):
     (1, 17, 1, 128, False),
     (3, 64, 2, 128, True),
     (1, 2000, 1, 64, True),
+    (1, 600, 2, 128, True),     # three 256-row blocks: one causal workgroup takes a single block
+    (1, 600, 1, 64, False),
+    (1, 260, 1, 128, True),     # last block holds 4 rows: three of its waves have no rows
+    (2, 1500, 1, 128, True),    # six blocks, ragged last key tile
 ])
 def test_fwd_bf16(B, N, H, d, causal):
     qb, kb, vb = gen_dense(2, B, N, H, d, "bf16")
