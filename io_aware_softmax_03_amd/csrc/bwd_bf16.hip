@@ -111,11 +111,23 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
   __shared__ __attribute__((aligned(16))) float s_lse[2][kBQ];
   __shared__ __attribute__((aligned(16))) float s_dlt[2][kBQ];
 
+  // Work decode, XCD-aware (workgroup w runs on XCD w % 8): each XCD takes a contiguous
+  // range of batch*head (so K, V, Q and dO of a head share its L2), and within it the key
+  // blocks go in order of decreasing work (causal: low key blocks see the most queries),
+  // all heads' first block before any head's second.
   const int total = p.grid;
   const int w = group_id_x();
-  const int logical = (total % 8 == 0) ? (w % 8) * (total / 8) + (w / 8) : w;
-  const int kb = logical % p.nkb;             // causal: low key blocks (most work) first
-  const int bh = logical / p.nkb;
+  int kb, bh;
+  const int nbh = total / p.nkb;
+  if (total % 8 == 0 && nbh % 8 == 0) {
+    const int per = nbh / 8;              // heads per XCD
+    const int slot = w / 8;
+    kb = slot / per;
+    bh = (w % 8) * per + slot % per;
+  } else {
+    kb = w % p.nkb;
+    bh = w / p.nkb;
+  }
   const int h = bh % p.heads, b = bh / p.heads;
   const int N = p.seqlen;
   const size_t rs = (size_t)p.heads * D;
@@ -148,6 +160,22 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
     u32x4 x = {0u, 0u, 0u, 0u};
     if (key < N) x = *(const u32x4*)(p.k + base + (size_t)key * rs + c * 8);
     *(u32x4*)(s_k + row * D + ((c ^ swz_tr<D>(row)) << 3)) = x;
+  }
+
+  // The K operands of dQ = dS K for this wave's head dims are the same for every query
+  // block: read them from LDS once (transpose reads), after the block is staged.
+  constexpr int QCOLS = D / kNW;  // head dims of dQ per wave (32 for D = 128, 16 for D = 64)
+  __syncthreads();
+  bf16x8 kq[kBK / 16];
+#pragma unroll
+  for (int ks = 0; ks < kBK / 16; ++ks) {
+    const int row_a = 16 * ks + 4 * hh + (gi >> 2);
+    const int row_b = row_a + 8;
+    int col = wid * QCOLS + 16 * nh + 4 * (gi & 3);
+    if (QCOLS == 16) col = wid * QCOLS + 4 * (gi & 3);  // D = 64: lanes 16-31 repeat
+    const int ca = (((col >> 3) ^ swz_tr<D>(row_a)) << 3) + (col & 7);
+    const int cb = (((col >> 3) ^ swz_tr<D>(row_b)) << 3) + (col & 7);
+    kq[ks] = join_tr(lds_read_tr(s_k + row_a * D + ca), lds_read_tr(s_k + row_b * D + cb));
   }
 
   f32x16 dk_acc[DB], dv_acc[DB];
@@ -280,7 +308,6 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
 
     // dQ_i[:, cols of this wave] = scale * dS K over the 128 keys of the block
     {
-      constexpr int QCOLS = D / kNW;  // head dims per wave (32 for D = 128, 16 for D = 64)
       f32x16 dq_acc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) dq_acc[i] = 0.f;
@@ -294,13 +321,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
         const int qc = 16 * nh + 4 * (gi & 3);
         const bf16x8 ads = join_tr(lds_read_tr(s_ds + row_a * kDsStride + qc),
                                    lds_read_tr(s_ds + row_b * kDsStride + qc));
-        // B = K (keys x dims): transpose read of K rows (keys), columns (dims)
-        int col = wid * QCOLS + 16 * nh + 4 * (gi & 3);
-        if (QCOLS == 16) col = wid * QCOLS + 4 * (gi & 3) + 16 * 0;  // D = 64: lanes 16-31 repeat
-        const int ca = (((col >> 3) ^ swz_tr<D>(row_a)) << 3) + (col & 7);
-        const int cb = (((col >> 3) ^ swz_tr<D>(row_b)) << 3) + (col & 7);
-        const bf16x8 bk = join_tr(lds_read_tr(s_k + row_a * D + ca), lds_read_tr(s_k + row_b * D + cb));
-        dq_acc = mfma32(ads, bk, dq_acc);
+        dq_acc = mfma32(ads, kq[ks], dq_acc);
       }
       // lane holds dQ[query 8i + 4hh + j][dim wid*QCOLS + r]
       if (QCOLS == 32 || r < 16) {
