@@ -101,7 +101,8 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
                   const int* cu_seqlens, int num_seqs, int total_tokens, int max_seqlen,
                   int H, int d, float scale, int causal, int dtype, void* stream);
 
-/* Bytes of workspace fa_bwd needs: the row statistic D = rowsum(dO * O), fp32 [B, H, N]. */
+/* Bytes of workspace fa_bwd needs: the row statistic D = rowsum(dO * O) and the LSE in base 2
+ * (LSE * log2(e)), each fp32 [B, H, N]. */
 size_t fa_bwd_workspace_bytes(int B, int H, int N);
 
 /*

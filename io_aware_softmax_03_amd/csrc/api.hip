@@ -87,7 +87,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N) {
   if (B < 0 || H < 0 || N < 0) return 0;
-  return (size_t)B * H * N * sizeof(float);
+  return 2 * (size_t)B * H * N * sizeof(float);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,

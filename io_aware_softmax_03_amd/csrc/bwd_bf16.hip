@@ -6,17 +6,19 @@
 // backward is parallel over key blocks, dK_j and dV_j belong to one block, dQ_i is
 // accumulated with atomic additions in device memory).
 //
-// Kernel 1 (preprocess): D_i = sum_c dO_ic O_ic per row, and dQ <- 0.
+// Kernel 1 (preprocess): D_i = sum_c dO_ic O_ic per row, LSE_i * log2(e), and dQ <- 0.
 // Kernel 2 (main): one workgroup per (128-key block, batch*head); each of its 4 waves owns
 // 32 keys and keeps K, V (as MFMA operands) and dK, dV (fp32 accumulators) in registers.
-// It walks 32-query blocks (causal: only those that can see a key of the block), staged
-// in LDS with the next block's loads in flight:
+// It walks 32-query blocks (causal: only those that can see a key of the block); the Q and
+// dO tiles go from HBM straight into LDS (buffer loads, one block ahead, double buffered):
 //   S  = Q K^T            (queries x keys; one key per lane, 16 queries per lane)
 //   P  = exp2(S*c - LSE2) , dP = dO V^T , dS = P * (dP - D)
 //   dV += P^T dO ,  dK += dS^T Q   (P, dS straight from registers; dO, Q transposed by
 //                                   the LDS transpose read)
-//   dS^T goes to LDS; then each wave forms 32 of the head dims of dQ_i = dS K over all
-//   128 keys of the block and adds them into dQ with one fp32 atomic per element.
+//   dS^T goes to LDS (double buffered); in the next step each wave forms 32 of the head dims
+//   of dQ_i = dS K over all 128 keys of the block, with its MFMAs running beside the
+//   exponentials of that step, and adds them into dQ with one fp32 atomic per element.
+// One workgroup barrier per query block.
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -26,12 +28,13 @@ namespace {
 constexpr int kNW = 4;          // waves per workgroup
 constexpr int kBK = 32 * kNW;   // keys per workgroup
 constexpr int kBQ = 32;         // queries per step
-constexpr int kDsStride = 36;   // dS^T row stride in elements (72 bytes, conflict-free writes)
+constexpr int kDsStride = 32;   // dS^T row stride in elements (64 bytes; 8-byte groups swizzled)
 
 struct PreArgs {
   const uint16_t* o;
   const uint16_t* dout;
-  float* delta;
+  const float* lse;
+  float* delta;  // D, then LSE * log2(e)
   float* dq;
   int heads, seqlen;
   long long rows;  // B * N * H
@@ -65,7 +68,9 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(PreArgs p) {
     const long long bn = row / p.heads;
     const int n = (int)(bn % p.seqlen);
     const long long b = bn / p.seqlen;
-    p.delta[((size_t)b * p.heads + h) * p.seqlen + n] = acc;
+    const size_t i = ((size_t)b * p.heads + h) * p.seqlen + n;
+    p.delta[i] = acc;
+    p.delta[(size_t)p.rows + i] = p.lse[i] * kLog2e;
   }
 }
 
@@ -80,13 +85,25 @@ struct MainArgs {
   float* dk;
   float* dv;
   int heads, seqlen, nkb;
-  int grid;  // workgroups launched
+  int grid;         // workgroups launched
+  long long rows;   // B * H * N: offset of the base-2 LSE in the workspace
   float scale, scale_log2;
 };
 
+// Q and dO tiles are read two ways: 16 consecutive rows at one 16-byte chunk
+// (ds_read_b128, operands of S and dP) and 4 consecutive rows x 4 consecutive chunks (the
+// transpose read, operands of dV and dK). XOR-ing the chunk index with this function of the
+// row keeps both conflict-free: over 16 rows it takes 16 distinct values (8 for D = 64, per
+// row parity), and over 4 aligned rows it differs in the chunk bits the 4 chunks do not use.
 template <int D>
-__device__ __forceinline__ int swz_row(int row) {  // rows read 32 at a time by ds_read_b128
-  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+__device__ __forceinline__ int swz_row(int row) {
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+// dS^T element (row = key, col = query): 64-byte rows whose 8-byte groups are XOR-ed with
+// (row / 4) % 8, so the row-wise writes (32 keys at one column group) and the transpose
+// reads (4 consecutive keys x all 32 queries) are both conflict-free.
+__device__ __forceinline__ int ds_off(int row, int col) {
+  return row * kDsStride + ((((col >> 2) ^ (row >> 2)) & 7) << 2) + (col & 3);
 }
 template <int D>
 __device__ __forceinline__ int swz_tr(int row) {   // rows read 8 at a time by the transpose read
@@ -100,16 +117,22 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
   constexpr int QT = kBQ * D;                 // elements of a Q or dO tile
-  constexpr int LOADS = kBQ * CH / NT;        // 16-byte chunks per thread per tile
-  static_assert(kBQ * CH % NT == 0, "tile split");
+  constexpr int TILE_B = QT * 2;              // bytes of one Q or dO tile
+  constexpr int ROWS_PER_KB = 1024 / (2 * D);
+  constexpr int LOADS = TILE_B / 1024 / kNW;  // 1 KB wave-loads per tile per wave
+  static_assert(TILE_B % (1024 * kNW) == 0, "tile split");
   static_assert(D / 32 == kNW || D == 64, "dQ head-dim split assumes D = 32 * waves (or D = 64)");
 
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[kBK * D];          // K block (transpose reads)
-  __shared__ __attribute__((aligned(16))) uint16_t s_q[2][QT];             // Q tiles
-  __shared__ __attribute__((aligned(16))) uint16_t s_do[2][QT];            // dO tiles
-  __shared__ __attribute__((aligned(16))) uint16_t s_ds[kBK * kDsStride];  // dS^T [key][query]
-  __shared__ __attribute__((aligned(16))) float s_lse[2][kBQ];
-  __shared__ __attribute__((aligned(16))) float s_dlt[2][kBQ];
+  // Q and dO tiles as separate LDS objects per buffer: each access names its buffer at
+  // compile time, so a copy into one buffer does not make reads of the other wait.
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[kBK * D];            // K block (transpose reads)
+  // (each Q buffer also holds its tile's base-2 LSE and D: 2 x 32 floats after the tile, so
+  // that every copy target is a Q or dO buffer)
+  __shared__ __attribute__((aligned(1024))) uint16_t s_q0[QT + 4 * kBQ];     // Q tiles
+  __shared__ __attribute__((aligned(1024))) uint16_t s_q1[QT + 4 * kBQ];
+  __shared__ __attribute__((aligned(1024))) uint16_t s_do0[QT];              // dO tiles
+  __shared__ __attribute__((aligned(1024))) uint16_t s_do1[QT];
+  __shared__ __attribute__((aligned(16))) uint16_t s_ds[2][kBK * kDsStride];  // dS^T [key][query]
 
   // Work decode, XCD-aware (workgroup w runs on XCD w % 8): each XCD takes a contiguous
   // range of batch*head (so K, V, Q and dO of a head share its L2), and within it the key
@@ -132,8 +155,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
   const int N = p.seqlen;
   const size_t rs = (size_t)p.heads * D;
   const size_t base = ((size_t)b * N * p.heads + h) * D;
-  const float* lse_g = p.lse + ((size_t)b * p.heads + h) * N;
   const float* dlt_g = p.delta + ((size_t)b * p.heads + h) * N;
+  const float* lse_g = p.delta + (size_t)p.rows + ((size_t)b * p.heads + h) * N;  // base-2 LSE
 
   const int tid = thread_id_x(), wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5, nh = r >> 4, gi = lane & 15;
@@ -187,154 +210,198 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
   const int qstart = CAUSAL ? kb0 : 0;   // first query that can see a key of the block
   const int nsteps = (N - qstart + kBQ - 1) / kBQ;
 
-  u32x4 qreg[LOADS], doreg[LOADS];
-  float lreg = 0.f, dreg = 0.f;
-  auto load_step = [&](int st) {
-    const int q0 = qstart + st * kBQ;
+  // ---- tile copies: wave-load `it` of this wave fills tile rows
+  // (wid*LOADS + it)*ROWS_PER_KB + lane/CH at physical chunk lane%CH with the logical chunk
+  // the row swizzle puts there; the buffer resource ends with the sequence, so rows past it
+  // arrive as zeros (their LSE is +inf below, so their P and dS are 0).
+  unsigned t_src[LOADS];
 #pragma unroll
-    for (int it = 0; it < LOADS; ++it) {
-      const int ci = tid + it * NT;
-      const int row = ci / CH, c = ci % CH;
-      const int qi = q0 + row;
-      u32x4 zq = {0u, 0u, 0u, 0u}, zd = {0u, 0u, 0u, 0u};
-      if (qi < N) {
-        zq = *(const u32x4*)(p.q + base + (size_t)qi * rs + c * 8);
-        zd = *(const u32x4*)(p.dout + base + (size_t)qi * rs + c * 8);
-      }
-      qreg[it] = zq;
-      doreg[it] = zd;
-    }
-    if (tid < kBQ) {
-      const int qi = q0 + tid;
-      lreg = qi < N ? lse_g[qi] * kLog2e : INFINITY;  // invalid rows get P = 0
-      dreg = qi < N ? dlt_g[qi] : 0.f;
-    }
-  };
-  auto store_step = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < LOADS; ++it) {
-      const int ci = tid + it * NT;
-      const int row = ci / CH, c = ci % CH;
-      *(u32x4*)(&s_q[buf][row * D + ((c ^ swz_row<D>(row)) << 3)]) = qreg[it];
-      *(u32x4*)(&s_do[buf][row * D + ((c ^ swz_row<D>(row)) << 3)]) = doreg[it];
-    }
-    if (tid < kBQ) {
-      s_lse[buf][tid] = lreg;
-      s_dlt[buf][tid] = dreg;
-    }
-  };
-
-  if (nsteps > 0) {
-    load_step(0);
-    store_step(0);
+  for (int it = 0; it < LOADS; ++it) {
+    const int lrow = (wid * LOADS + it) * ROWS_PER_KB + lane / CH;
+    t_src[it] = (unsigned)(lrow * (int)rs + ((lane % CH) ^ swz_row<D>(lrow)) * 8) * 2u;
   }
-  __syncthreads();
-
-  for (int st = 0; st < nsteps; ++st) {
-    const int buf = st & 1;
+  auto issue_tile = [&](auto bufc, int st) {
     const int q0 = qstart + st * kBQ;
-    if (st + 1 < nsteps) load_step(st + 1);
-    const uint16_t* sq = s_q[buf];
-    const uint16_t* sd = s_do[buf];
+    const unsigned bytes = (unsigned)(min(kBQ - 1, N - 1 - q0) * (int)rs + D) * 2u;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + base + (size_t)q0 * rs, bytes);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.dout + base + (size_t)q0 * rs, bytes);
+    uint16_t* dq_ = decltype(bufc)::value ? s_q1 : s_q0;
+    uint16_t* dd_ = decltype(bufc)::value ? s_do1 : s_do0;
+#pragma unroll
+    for (int it = 0; it < LOADS; ++it) {
+      const int off = (wid * LOADS + it) * 1024;  // this wave-load's 1 KB slice of the tile
+      copy16_to_lds(rq, t_src[it], (char*)dq_ + off);
+      copy16_to_lds(rd, t_src[it], (char*)dd_ + off);
+    }
+    // the tile's base-2 LSE and D, 4 bytes per lane of wave 0 (rows past the end read 0: their
+    // Q and dO rows are 0 too, so P = 1 there multiplies zero rows and dS = 0)
+    if (wid == 0 && lane < kBQ) {
+      const unsigned fb = (unsigned)min(kBQ, N - q0) * 4u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(lse_g + q0, fb), (lds_void*)(dq_ + QT), 4, 4u * lane, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(dlt_g + q0, fb), (lds_void*)(dq_ + QT + 2 * kBQ), 4, 4u * lane, 0, 0, 0);
+    }
+  };
 
-    const bool active = myk - r < N && (!CAUSAL || q0 + kBQ - 1 >= kw);
-    f32x16 pr, ds;  // P and dS, lane = key r, acc[4i+j] = query 8i + 4hh + j
-    if (active) {
-      f32x16 s, dp;
+  f32x16 dq_acc;  // dQ of the previous query block: lane holds [query 8i + 4hh + j][dim wid*QCOLS + r]
+  // dQ_{i} of this wave's head dims = dS_i K over the 128 keys of the block (dS^T from LDS)
+  auto dq_mfma = [&](auto bufc, int q0) {
+    const uint16_t* sds = s_ds[decltype(bufc)::value];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) { s[i] = 0.f; dp[i] = 0.f; }
+    for (int i = 0; i < 16; ++i) dq_acc[i] = 0.f;
+    const int kmax = CAUSAL ? min(kBK, q0 + kBQ - kb0) : kBK;  // keys past the last query give dS = 0
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const int c = 2 * kk + hh;
-        const bf16x8 aq = __builtin_bit_cast(bf16x8, *(const u32x4*)(sq + r * D + ((c ^ swz_row<D>(r)) << 3)));
-        const bf16x8 ad = __builtin_bit_cast(bf16x8, *(const u32x4*)(sd + r * D + ((c ^ swz_row<D>(r)) << 3)));
-        s = mfma32(aq, kf[kk], s);
-        dp = mfma32(ad, vf[kk], dp);
-      }
-      const bool edge = (CAUSAL && q0 < kw + 31) || (q0 + kBQ > N) || (kw + 32 > N);
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 l4 = *(const f32x4*)(&s_lse[buf][8 * i4 + 4 * hh]);
-        const f32x4 d4 = *(const f32x4*)(&s_dlt[buf][8 * i4 + 4 * hh]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = 4 * i4 + j;
-          float pv = exp2_fast(__builtin_fmaf(s[i], p.scale_log2, -l4[j]));
-          if (edge) {
-            const int qi = q0 + 8 * i4 + 4 * hh + j;
-            if ((CAUSAL && myk > qi) || myk >= N) pv = 0.f;
-          }
-          pr[i] = pv;
-          ds[i] = pv * (dp[i] - d4[j]);
-        }
-      }
-      // dV += P^T dO, dK += dS^T Q  (k-step ks: queries 16ks + 8(e/4) + 4hh + e%4)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int o8 = 8 * ks;
-        const bf16x8 ap = pack_bf16x8(pr[o8], pr[o8 + 1], pr[o8 + 2], pr[o8 + 3],
-                                      pr[o8 + 4], pr[o8 + 5], pr[o8 + 6], pr[o8 + 7]);
-        const bf16x8 as = pack_bf16x8(ds[o8], ds[o8 + 1], ds[o8 + 2], ds[o8 + 3],
-                                      ds[o8 + 4], ds[o8 + 5], ds[o8 + 6], ds[o8 + 7]);
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      if (16 * ks < kmax) {
         const int row_a = 16 * ks + 4 * hh + (gi >> 2);
         const int row_b = row_a + 8;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int col = db * 32 + 16 * nh + 4 * (gi & 3);
-          const int ca = (((col >> 3) ^ swz_row<D>(row_a)) << 3) + (col & 7);
-          const int cb = (((col >> 3) ^ swz_row<D>(row_b)) << 3) + (col & 7);
-          const bf16x8 bdo = join_tr(lds_read_tr(sd + row_a * D + ca), lds_read_tr(sd + row_b * D + cb));
-          const bf16x8 bq = join_tr(lds_read_tr(sq + row_a * D + ca), lds_read_tr(sq + row_b * D + cb));
-          dv_acc[db] = mfma32(ap, bdo, dv_acc[db]);
-          dk_acc[db] = mfma32(as, bq, dk_acc[db]);
-        }
+        const int qc = 16 * nh + 4 * (gi & 3);
+        const bf16x8 ads = join_tr(lds_read_tr(sds + ds_off(row_a, qc)), lds_read_tr(sds + ds_off(row_b, qc)));
+        dq_acc = mfma32(ads, kq[ks], dq_acc);
       }
-    } else {
+    }
+  };
+  // Exactly kDqAtomics atomic instructions per call (rows past the end add 0 to the last
+  // row), so the step's wait can leave them in flight: see step_sync.
+  auto dq_atomics = [&](int q0) {
+    if (QCOLS == 32 || r < 16) {
+      float* dqg = p.dq + base + wid * QCOLS + r;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ds[i] = 0.f;
+      for (int i = 0; i < 16; ++i) {
+        const int qi = q0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+        const float x = qi < N ? dq_acc[i] * p.scale : 0.f;
+        atomicAdd(dqg + (size_t)min(qi, N - 1) * rs, x);
+      }
+    }
+  };
+  // End of a step: the tile copies of this step have landed and its LDS accesses are done,
+  // then the workgroup barrier. Vector memory operations retire in issue order and the dQ
+  // atomics of the step (if any) were issued after the copies, so waiting until at most
+  // that many remain leaves the atomics in flight. The barrier is a bare s_barrier: the
+  // fences of __syncthreads() (and the compiler's handling of the barrier builtin) would
+  // wait for all of them.
+  constexpr int kDqAtomics = 16;
+  auto step_sync = [&](bool atomics_issued) {
+    // s_waitcnt immediate: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
+    constexpr int kWaitAtomics = (kDqAtomics & 15) | ((kDqAtomics >> 4) << 14) | (0x7 << 4) | (0x0 << 8);
+    if (atomics_issued)
+      __builtin_amdgcn_s_waitcnt(kWaitAtomics);  // vmcnt(16) lgkmcnt(0)
+    else
+      __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("s_barrier" ::: "memory");
+  };
+
+  // prologue: tile 0, its LSE and D; dS^T buffer 1 cleared (the first step's dQ MFMAs read
+  // it, and their zero result is not added anywhere)
+  if (nsteps > 0) issue_tile(std::integral_constant<int, 0>(), 0);
+  for (int e = tid; e < kBK * kDsStride / 2; e += NT) ((uint32_t*)s_ds[1])[e] = 0u;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // step st (buffer parity B = st & 1): copies of tile st+1; S, dP of tile st; P, dS beside
+  // the dQ MFMAs of tile st-1; dS^T of tile st to LDS; dV, dK; atomics of dQ of tile st-1
+  auto step = [&](auto bufc, int st) {
+    constexpr int B = decltype(bufc)::value;
+    using NB = std::integral_constant<int, B ^ 1>;
+    const int q0 = qstart + st * kBQ;
+    if (st + 1 < nsteps) issue_tile(NB(), st + 1);
+    const uint16_t* sq = B ? s_q1 : s_q0;
+    const uint16_t* sd = B ? s_do1 : s_do0;
+
+    f32x16 sc, dp;  // S and dP: lane = key r, acc[4i+j] = query 8i + 4hh + j
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int c = 2 * kk + hh;
+      const bf16x8 aq = __builtin_bit_cast(bf16x8, *(const u32x4*)(sq + r * D + ((c ^ swz_row<D>(r)) << 3)));
+      const bf16x8 ad = __builtin_bit_cast(bf16x8, *(const u32x4*)(sd + r * D + ((c ^ swz_row<D>(r)) << 3)));
+      sc = mfma32(aq, kf[kk], kk == 0 ? f32x16{} : sc);
+      dp = mfma32(ad, vf[kk], kk == 0 ? f32x16{} : dp);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const bool edge = (CAUSAL && q0 < kw + 31) || (q0 + kBQ > N) || (kw + 32 > N);
+    if (edge) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int qi = q0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+        if ((CAUSAL && myk > qi) || myk >= N) sc[i] = -INFINITY;
+      }
+    }
+    // P, dS of this tile beside the dQ MFMAs of the previous tile
+    dq_mfma(NB(), q0 - kBQ);
+    f32x16 pr, ds;
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const f32x4 l4 = *(const f32x4*)((const float*)(sq + QT) + 8 * i4 + 4 * hh);
+      const f32x4 d4 = *(const f32x4*)((const float*)(sq + QT + 2 * kBQ) + 8 * i4 + 4 * hh);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * i4 + j;
+        pr[i] = exp2_fast(__builtin_fmaf(sc[i], p.scale_log2, -l4[j]));
+        ds[i] = pr[i] * (dp[i] - d4[j]);
+      }
+    }
+    bf16x8 ap[2], as[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int o8 = 8 * ks;
+      ap[ks] = pack_bf16x8(pr[o8], pr[o8 + 1], pr[o8 + 2], pr[o8 + 3], pr[o8 + 4], pr[o8 + 5], pr[o8 + 6], pr[o8 + 7]);
+      as[ks] = pack_bf16x8(ds[o8], ds[o8 + 1], ds[o8 + 2], ds[o8 + 3], ds[o8 + 4], ds[o8 + 5], ds[o8 + 6], ds[o8 + 7]);
     }
     // dS^T -> LDS: row = key (32*wid + r), columns = queries 8i + 4hh + 0..3
     {
-      uint16_t* dst = s_ds + (32 * wid + r) * kDsStride + 4 * hh;
+      // (written with inline ds_write_b64: for the C++ stores the compiler waits for the tile
+      // copies in flight, not knowing they target other LDS buffers; the step's closing
+      // lgkmcnt(0) orders these writes before the barrier)
+      const unsigned dst = (unsigned)(uintptr_t)(const void*)s_ds[B];
+      const int row = 32 * wid + r;
+      const u32x4 w0 = __builtin_bit_cast(u32x4, as[0]), w1 = __builtin_bit_cast(u32x4, as[1]);
+      const u32x2 v0 = {w0[0], w0[1]}, v1 = {w0[2], w0[3]}, v2 = {w1[0], w1[1]}, v3 = {w1[2], w1[3]};
+      asm volatile("ds_write_b64 %0, %1" ::"v"(dst + 2u * ds_off(row, 0 + 4 * hh)), "v"(v0) : "memory");
+      asm volatile("ds_write_b64 %0, %1" ::"v"(dst + 2u * ds_off(row, 8 + 4 * hh)), "v"(v1) : "memory");
+      asm volatile("ds_write_b64 %0, %1" ::"v"(dst + 2u * ds_off(row, 16 + 4 * hh)), "v"(v2) : "memory");
+      asm volatile("ds_write_b64 %0, %1" ::"v"(dst + 2u * ds_off(row, 24 + 4 * hh)), "v"(v3) : "memory");
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        u32x2 wv;
-        wv[0] = pack_bf16x2(ds[4 * i4 + 0], ds[4 * i4 + 1]);
-        wv[1] = pack_bf16x2(ds[4 * i4 + 2], ds[4 * i4 + 3]);
-        *(u32x2*)(dst + 8 * i4) = wv;
+    for (int i = 0; i < 7; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (st > 0) dq_atomics(q0 - kBQ);  // the dQ MFMAs have finished by now
+    // dV += P^T dO, dK += dS^T Q  (k-step ks: queries 16ks + 8(e/4) + 4hh + e%4)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int row_a = 16 * ks + 4 * hh + (gi >> 2);
+      const int row_b = row_a + 8;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int col = db * 32 + 16 * nh + 4 * (gi & 3);
+        const int ca = (((col >> 3) ^ swz_row<D>(row_a)) << 3) + (col & 7);
+        const int cb = (((col >> 3) ^ swz_row<D>(row_b)) << 3) + (col & 7);
+        const bf16x8 bdo = join_tr(lds_read_tr(sd + row_a * D + ca), lds_read_tr(sd + row_b * D + cb));
+        const bf16x8 bq = join_tr(lds_read_tr(sq + row_a * D + ca), lds_read_tr(sq + row_b * D + cb));
+        dv_acc[db] = mfma32(ap[ks], bdo, dv_acc[db]);
+        dk_acc[db] = mfma32(as[ks], bq, dk_acc[db]);
       }
     }
-    __syncthreads();
-
-    // dQ_i[:, cols of this wave] = scale * dS K over the 128 keys of the block
-    {
-      f32x16 dq_acc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) dq_acc[i] = 0.f;
-      const int kmax = CAUSAL ? min(kBK, q0 + kBQ - kb0) : kBK;  // keys past the last query give dS = 0
-#pragma unroll
-      for (int ks = 0; ks < kBK / 16; ++ks) {
-        if (16 * ks >= kmax) break;
-        const int row_a = 16 * ks + 4 * hh + (gi >> 2);
-        const int row_b = row_a + 8;
-        // A = dS (queries x keys): transpose read of dS^T rows (keys), columns (queries)
-        const int qc = 16 * nh + 4 * (gi & 3);
-        const bf16x8 ads = join_tr(lds_read_tr(s_ds + row_a * kDsStride + qc),
-                                   lds_read_tr(s_ds + row_b * kDsStride + qc));
-        dq_acc = mfma32(ads, kq[ks], dq_acc);
-      }
-      // lane holds dQ[query 8i + 4hh + j][dim wid*QCOLS + r]
-      if (QCOLS == 32 || r < 16) {
-        float* dqg = p.dq + base + wid * QCOLS + r;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qi = q0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          if (qi < N) atomicAdd(dqg + (size_t)qi * rs, dq_acc[i] * p.scale);
-        }
-      }
-    }
-    if (st + 1 < nsteps) store_step(buf ^ 1);
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    step_sync(st > 0);
+  };
+  int st = 0;
+  for (; st + 1 < nsteps; st += 2) {
+    step(std::integral_constant<int, 0>(), st);
+    step(std::integral_constant<int, 1>(), st + 1);
+  }
+  if (st < nsteps) {
+    step(std::integral_constant<int, 0>(), st);
+    ++st;
+  }
+  // dQ of the last query block
+  if (nsteps > 0) {
+    if ((nsteps - 1) & 1) dq_mfma(std::integral_constant<int, 1>(), qstart + (nsteps - 1) * kBQ);
+    else dq_mfma(std::integral_constant<int, 0>(), qstart + (nsteps - 1) * kBQ);
+    dq_atomics(qstart + (nsteps - 1) * kBQ);
   }
 
   // dK = scale * dS^T Q, dV = P^T dO; lane holds [key 8i + 4hh + j][dim db*32 + r]
@@ -362,6 +429,7 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
   PreArgs pre;
   pre.o = (const uint16_t*)a.o;
   pre.dout = (const uint16_t*)a.dout;
+  pre.lse = a.lse;
   pre.delta = a.delta;
   pre.dq = a.dq;
   pre.heads = a.heads;
@@ -392,6 +460,7 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
   const long long blocks = (long long)m.nkb * a.batch * a.heads;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   m.grid = (int)blocks;
+  m.rows = pre.rows;
   return a.causal ? launch_main<D, true>(m, (int)blocks, stream) : launch_main<D, false>(m, (int)blocks, stream);
 }
 

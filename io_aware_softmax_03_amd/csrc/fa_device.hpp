@@ -125,4 +125,18 @@ __device__ __forceinline__ bf16x8 join_tr(const i16x4& lo, const i16x4& hi) {
   return __builtin_bit_cast(bf16x8, x);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer resource over `bytes` bytes at `base` (raw addressing, no stride).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// One wave-wide copy of 16 bytes per lane from a buffer into LDS (buffer_load_dwordx4 with
+// the LDS destination): lane i's bytes land at lds_wave_base + 16*i. The lane reads at byte
+// offset `off` of the buffer; offsets at or past the buffer's size read as zero.
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t src, unsigned off, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)lds_wave_base, 16, off, 0, 0, 0);
+}
+
 }  // namespace fa

@@ -35,7 +35,7 @@ struct BwdArgs {
   float* dq;
   float* dk;
   float* dv;
-  float* delta;  // workspace, [B, H, N]
+  float* delta;  // workspace: D [B, H, N], then LSE * log2(e) [B, H, N]
   int batch, heads, seqlen, head_dim;
   float scale;
   bool causal;

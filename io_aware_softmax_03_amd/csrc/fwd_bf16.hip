@@ -64,20 +64,6 @@ __device__ __forceinline__ int swz_v(int row) {
   return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// One wave-wide copy of 16 bytes per lane from a buffer into LDS (buffer_load_dwordx4 with
-// the LDS destination): lane i's bytes land at lds_wave_base + 16*i. The lane reads at byte
-// offset `off` of the buffer; offsets at or past the buffer's size read as zero.
-__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t src, unsigned off, void* lds_wave_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)lds_wave_base, 16, off, 0, 0, 0);
-}
-
-// Buffer resource over `bytes` bytes at `base` (raw addressing, no stride).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
-}
-
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
 // f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time

@@ -48,7 +48,7 @@ def test_strerror():
 
 def test_workspace_sizes():
     lib = _clib.lib()
-    assert lib.fa_bwd_workspace_bytes(4, 16, 4096) == 4 * 16 * 4096 * 4
+    assert lib.fa_bwd_workspace_bytes(4, 16, 4096) == 2 * 4 * 16 * 4096 * 4
     assert lib.fa_decode_workspace_bytes(64, 32, 128, 64) == 64 * 32 * 64 * 130 * 4
     assert lib.fa_bwd_workspace_bytes(-1, 1, 1) == 0
 
@@ -111,7 +111,7 @@ def bwd(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=_clib.FA_DTYPE_F32), _clib.FA_ERR_DTYPE), (dict(ws=None), _clib.FA_ERR_WORKSPACE),
-    (dict(ws_bytes=64 * 2 * 4 - 1), _clib.FA_ERR_WORKSPACE), (dict(dq=None), _clib.FA_ERR_NULL),
+    (dict(ws_bytes=2 * 64 * 2 * 4 - 1), _clib.FA_ERR_WORKSPACE), (dict(dq=None), _clib.FA_ERR_NULL),
     (dict(d=80), _clib.FA_ERR_HEADDIM), (dict(scale=float("inf")), _clib.FA_ERR_ARG),
     (dict(dk=FAKE + 4), _clib.FA_ERR_ARG), (dict(H=-2), _clib.FA_ERR_SHAPE),
 ])
