@@ -42,6 +42,9 @@ def run_bwd(seed, B, N, H, d, causal):
     (1, 300, 2, 64, False),
     (1, 1, 1, 128, True),
     (1, 33, 1, 128, False),
+    (2, 96, 2, 128, False),      # three query blocks per key block (odd step count)
+    (1, 700, 2, 128, True),      # six key blocks, query-block counts of both parities
+    (1, 513, 1, 64, True),
 ])
 def test_bwd_small(B, N, H, d, causal):
     (qb, kb, vb, gb), (dq, dk, dv) = run_bwd(4, B, N, H, d, causal)

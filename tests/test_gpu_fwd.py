@@ -59,6 +59,9 @@ def test_fwd_f32(B, N, H, d, causal):
     (1, 600, 1, 64, False),
     (1, 260, 1, 128, True),     # last block holds 4 rows: three of its waves have no rows
     (2, 1500, 1, 128, True),    # six blocks, ragged last key tile
+    (1, 300, 8, 64, True),      # head count divisible by 8: heads interleaved across XCDs
+    (2, 520, 8, 128, True),
+    (1, 777, 16, 128, False),
 ])
 def test_fwd_bf16(B, N, H, d, causal):
     qb, kb, vb = gen_dense(2, B, N, H, d, "bf16")
