@@ -11,7 +11,7 @@ the pages by eye:
 
 * ``attention``  — the definitions the GPU results are compared with:
   forward, packed variable-length forward, backward (exact gradient of the
-  forward), single-token decode.
+  forward), single-token decode, decode against a paged cache.
 * ``algorithms`` — the pages' algorithms written out step by step in float64
   (tiled online softmax, two-pass softmax, split-and-merge decoding, a scalar
   brute force). They exist to pin the definitions above and the pages' claims
@@ -26,7 +26,7 @@ backward, and the figures the pages print (``tests/golden``). No function is
 """
 from .attention import (  # noqa: F401
     attention_head, attn_fwd, attn_fwd_varlen, attn_bwd_head, attn_bwd,
-    attn_decode, attn_decode_slice,
+    attn_decode, attn_decode_slice, attn_decode_paged,
 )
 from .algorithms import (  # noqa: F401
     tiled_online_attention_head, softmax_two_pass, softmax_online,

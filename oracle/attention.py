@@ -152,3 +152,28 @@ def attn_decode(q, k_cache, v_cache, scale):
         for h in range(H):
             O[b, h], lse[b, h] = attn_decode_slice(q[b, h], kc[b, :, h], vc[b, :, h], scale)
     return O, lse
+
+
+def attn_decode_paged(q, k_pages, v_pages, block_table, seqlens, scale):
+    """Decode against a paged cache ("FlashAttention-2 and -3", "Paged KV caches, a preview
+    of serving"): the cache is a pool of fixed-size pages [num_pages, P, H, d] and row b of
+    the block table maps sequence b's logical blocks (tokens 0..P-1, P..2P-1, ...) to
+    physical pages. Token t of sequence b is page block_table[b, t // P], slot t % P.
+    Exactly seqlens[b] tokens are gathered (the slots past the end of the last page are not
+    part of the sequence), then the contiguous decode runs. An empty sequence gives O = 0,
+    LSE = -inf (a row with no visible key). q [B, H, d]; returns O [B, H, d], LSE [B, H]."""
+    q, kp, vp = _f64(q), _f64(k_pages), _f64(v_pages)
+    P = kp.shape[1]
+    B, H, _ = q.shape
+    O = np.zeros((B, H, vp.shape[3]))
+    lse = np.full((B, H), -np.inf)
+    for b in range(B):
+        L = int(seqlens[b])
+        if L == 0:
+            continue
+        t = np.arange(L)
+        pg, slot = block_table[b, t // P], t % P
+        k_rows, v_rows = kp[pg, slot], vp[pg, slot]  # [L, H, d]
+        for h in range(H):
+            O[b, h], lse[b, h] = attn_decode_slice(q[b, h], k_rows[:, h], v_rows[:, h], scale)
+    return O, lse

@@ -101,3 +101,37 @@ def decode_query(seed, B, H, d, dtype="bf16"):
         for h in range(H):
             out[b, h, :] = normal_slice(seed, TENSOR_Q, b, h, (d,))
     return _finish(out, dtype)
+
+
+def paged_layout(seed, seqlens, page_size, extra_pages=0):
+    """Block table for a paged cache: sequence b owns ceil(L_b / page_size) pages, listed in
+    row b of a [B, max_pages] int32 table; the physical pages are a seeded permutation of
+    the pool (plus `extra_pages` never referenced). Unused table entries point at random
+    valid pages. Returns (block_table, num_pages)."""
+    seqlens = [int(x) for x in seqlens]
+    need = [(L + page_size - 1) // page_size for L in seqlens]
+    max_pages = max(1, max(need) if need else 1)
+    num_pages = max(1, sum(need) + int(extra_pages))
+    rng = np.random.default_rng([seed, 77])
+    perm = rng.permutation(num_pages).astype(np.int32)
+    table = rng.integers(0, num_pages, size=(len(seqlens), max_pages)).astype(np.int32)
+    pos = 0
+    for b, n in enumerate(need):
+        table[b, :n] = perm[pos:pos + n]
+        pos += n
+    return table, num_pages
+
+
+def paged_tensor(seed, tensor_id, seqlens, block_table, num_pages, page_size, H, d, dtype="bf16"):
+    """Page pool [num_pages, page_size, H, d]: token t of sequence b (slice (b, h) of the
+    seeded normal draw, as in a contiguous cache) sits in page block_table[b, t // page_size]
+    at slot t % page_size. Every other slot holds seeded noise of its own."""
+    rng = np.random.default_rng([seed, tensor_id, 991])
+    pool = rng.standard_normal((num_pages, page_size, H, d)).astype(np.float32) * np.float32(3.0)
+    for b, L in enumerate(seqlens):
+        L = int(L)
+        for h in range(H):
+            x = normal_slice(seed, tensor_id, b, h, (L, d))
+            t = np.arange(L)
+            pool[block_table[b, t // page_size], t % page_size, h, :] = x
+    return _finish(pool, dtype)
