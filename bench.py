@@ -6,7 +6,8 @@ call over that batch, inputs resident in device memory). Reported as TFLOP/s by 
 convention 4*B*H*N^2*d/2 and as a fraction of the dense bf16 MFMA peak.
 
 Also measured in the same run (field "extra"): the backward (B=4, H=16, N=4096, d=128,
-causal), split-KV decode (B=64, H=32, L=32768, d=128, 64 splits), the packed varlen
+causal), split-KV decode (B=64, H=32, L=32768, d=128, 64 splits), the same decode over a
+paged cache (16-token pages, lengths 16384..32768), the packed varlen
 forward (16 sequences, H=32, d=64) and the fp32 forward (N=256, d=64); and the float64
 CPU oracle timed on a bounded sample of the headline workload (field "cpu_baseline").
 
@@ -189,6 +190,30 @@ def extra_measurements(steps):
                                              "frac_hbm_peak": round(nb / ev / 1e6 / PEAK_HBM_GBS, 4),
                                              "bytes_convention": "K and V caches read once + q + o"}
     del q, kc, vc, ws
+    torch.cuda.empty_cache()
+
+    # paged decode: B=64 H=32 d=128, 16-token pages scattered over the pool, lengths uniform
+    # in [16384, 32768], 64 splits
+    B, H, d, P = 64, 32, 128, 16
+    seqlens = synth.varlen_lengths(8, B, 16384, 32768).tolist()
+    table, num_pages = synth.paged_layout(8, seqlens, P, 0)
+    gen.manual_seed(8)
+    q = torch.randn((B, H, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+    kp = torch.randn((num_pages, P, H, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+    vp = torch.randn((num_pages, P, H, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+    tab = torch.from_numpy(table).to("cuda")
+    sl = torch.tensor(seqlens, dtype=torch.int32, device="cuda")
+    ws = torch.empty(fa.lib().fa_decode_workspace_bytes(B, H, d, 64), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    wall, ev, best = time_launches(
+        lambda: fa.decode_paged(q, kp, vp, tab, sl, num_splits=64, workspace=ws, out=(o, lse)),
+        max(3, steps // 2), 2)
+    nb = costs.decode_paged_bytes(seqlens, H, d)
+    out["decode_paged_b64_h32_p16_l16k_32k_d128_s64"] = {
+        "ms": round(ev, 4), "gbs": round(nb / ev / 1e6, 1), "frac_hbm_peak": round(nb / ev / 1e6 / PEAK_HBM_GBS, 4),
+        "tokens": int(sum(seqlens)), "bytes_convention": "valid K and V tokens read once + q + o"}
+    del q, kp, vp, ws
     torch.cuda.empty_cache()
     return out
 

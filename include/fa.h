@@ -149,6 +149,38 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, 
               int B, int H, int L, int d, float scale, int num_splits, int dtype,
               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fa_decode_paged — fa_decode over a paged KV cache ("FlashAttention-2 and -3",
+ * section "Paged KV caches, a preview of serving"): keys and values live in a
+ * pool of fixed-size pages, and a per-sequence block table maps logical block
+ * j (tokens j*page_size .. (j+1)*page_size - 1) to a physical page. The kernel
+ * gathers whole pages; the split over keys and the merge are those of
+ * fa_decode, with each sequence cut into num_splits chunks of
+ * ceil(seqlens[b] / num_splits) keys.
+ *   q           [B, H, d]
+ *   k_pages,
+ *   v_pages     [num_pages, page_size, H, d]
+ *   block_table int32 [B, max_pages], row-major; entry j of row b is the page
+ *               holding tokens j*page_size .. of sequence b. Entries past the
+ *               sequence's last page are never read.
+ *   seqlens     int32 [B]: tokens cached for each sequence, 0 .. max_pages *
+ *               page_size. Slots past seqlens[b] in its last page are ignored.
+ *   o           [B, H, d] (written); a sequence with no tokens gets zeros
+ *   lse         fp32 [B, H] (written) or NULL; -inf for a sequence with no tokens
+ *   page_size   a power of two, 1 .. 1024; max_pages * page_size <= 2^30
+ *   workspace   at least fa_decode_workspace_bytes(B, H, d, num_splits) bytes
+ * All pointers are device pointers; block_table and seqlens are read on the
+ * device (4-byte aligned), the rest need 16-byte alignment. The kernel clamps
+ * seqlens to [0, max_pages * page_size] and page ids to [0, num_pages - 1], so
+ * bad table contents give wrong values, never reads outside the buffers; they
+ * are not reported as errors. Only FA_DTYPE_BF16.
+ */
+int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                    const int* block_table, const int* seqlens, void* o, float* lse,
+                    int B, int H, int d, int page_size, int num_pages, int max_pages,
+                    float scale, int num_splits, int dtype,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,6 +9,7 @@ memory and streams. Tensors must be contiguous device tensors:
     fwd_varlen(q, k, v, cu_seqlens, max_seqlen, ...) -> (o, lse) q,k,v [T, H, d]
     bwd(q, k, v, o, lse, do, scale=None, causal=False) -> (dq, dk, dv)   fp32 grads
     decode(q, k_cache, v_cache, scale=None, num_splits=64) -> (o, lse)   q [B, H, d]
+    decode_paged(q, k_pages, v_pages, block_table, seqlens, ...) -> (o, lse)
 
 ``scale`` defaults to 1/sqrt(d).
 """
@@ -20,7 +21,7 @@ from ._clib import (  # noqa: F401
     FAError, FA_DTYPE_BF16, FA_DTYPE_F32, check, lib, strerror,
 )
 
-__all__ = ["fwd", "fwd_varlen", "bwd", "decode", "FAError", "lib"]
+__all__ = ["fwd", "fwd_varlen", "bwd", "decode", "decode_paged", "FAError", "lib"]
 
 
 def _torch():
@@ -155,4 +156,39 @@ def decode(q, k_cache, v_cache, scale=None, num_splits=64, workspace=None, out=N
                          B, H, L, d, _scale(scale, d), num_splits, _dtype_code(q),
                          workspace.data_ptr(), workspace.numel(), _stream(q.device))
     check(st, "fa_decode")
+    return o, lse
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seqlens, scale=None, num_splits=64, workspace=None, out=None):
+    """Single-token decode over a paged cache. q [B, H, d]; pages [num_pages, page_size, H, d];
+    block_table int32 [B, max_pages]; seqlens int32 [B]. Returns O [B, H, d], LSE [B, H]."""
+    torch = _torch()
+    _require((q, k_pages, v_pages, block_table, seqlens), ("q", "k_pages", "v_pages", "block_table", "seqlens"))
+    B, H, d = q.shape
+    num_pages, page_size = k_pages.shape[0], k_pages.shape[1]
+    if k_pages.shape != (num_pages, page_size, H, d) or v_pages.shape != k_pages.shape:
+        raise ValueError("pages must be [num_pages, page_size, H, d] matching q")
+    if k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
+        raise TypeError("q and the pages must share a dtype")
+    if block_table.dtype != torch.int32 or seqlens.dtype != torch.int32:
+        raise TypeError("block_table and seqlens must be int32")
+    if block_table.dim() != 2 or block_table.shape[0] != B or seqlens.shape != (B,):
+        raise ValueError("block_table must be [B, max_pages] and seqlens [B]")
+    max_pages = block_table.shape[1]
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        _require((o, lse), ("o", "lse"))
+        if o.shape != q.shape or o.dtype != q.dtype or lse.shape != (B, H) or lse.dtype != torch.float32:
+            raise ValueError("out must be (o [B, H, d] like q, lse fp32 [B, H])")
+    nbytes = lib().fa_decode_workspace_bytes(B, H, d, num_splits)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    st = lib().fa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
+                               seqlens.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, d, page_size, num_pages,
+                               max_pages, _scale(scale, d), num_splits, _dtype_code(q),
+                               workspace.data_ptr(), workspace.numel(), _stream(q.device))
+    check(st, "fa_decode_paged")
     return o, lse

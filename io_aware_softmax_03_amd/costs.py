@@ -38,6 +38,16 @@ def decode_bytes(B, H, L, d, elem_bytes=2):
     return 2.0 * B * L * H * d * elem_bytes + 2.0 * B * H * d * elem_bytes
 
 
+def decode_paged_bytes(seqlens, H, d, elem_bytes=2, table_bytes=0):
+    """Compulsory HBM bytes of one paged decode step: each sequence's valid K and V tokens
+    read once, plus q and o, plus the block-table entries read ("Paged KV caches, a
+    preview of serving": the gather touches only the pages a sequence owns)."""
+    seqlens = list(seqlens)
+    tokens = sum(seqlens)
+    B = len(seqlens)
+    return 2.0 * tokens * H * d * elem_bytes + 2.0 * B * H * d * elem_bytes + table_bytes
+
+
 def fwd_compulsory_bytes(B, H, N, d, elem_bytes=2):
     """Q, K, V read once, O written once, fp32 LSE written once."""
     return 4.0 * B * N * H * d * elem_bytes + 4.0 * B * H * N

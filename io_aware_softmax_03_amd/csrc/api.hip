@@ -11,6 +11,7 @@ namespace {
 
 constexpr long long kMaxElems = 1LL << 62;
 constexpr int kMaxSplits = 1024;
+constexpr int kMaxPageSize = 1024;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
@@ -125,7 +126,33 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, 
   if (!q || !k_cache || !v_cache || !o) return FA_ERR_NULL;
   if (!workspace || workspace_bytes < fa_decode_workspace_bytes(B, H, d, num_splits)) return FA_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace)) return FA_ERR_ARG;
-  fa::DecodeArgs a{q, k_cache, v_cache, o, lse, (float*)workspace, B, H, L, d, num_splits, scale};
+  fa::DecodeArgs a{q, k_cache, v_cache, o, lse, (float*)workspace, B, H, L, d, num_splits, scale,
+                   nullptr, nullptr, 0, 0, 0};
+  return from_hip(fa::launch_decode_bf16(a, (hipStream_t)stream));
+}
+
+int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int* block_table,
+                    const int* seqlens, void* o, float* lse, int B, int H, int d, int page_size,
+                    int num_pages, int max_pages, float scale, int num_splits, int dtype, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (B < 0 || H <= 0 || num_pages <= 0 || max_pages <= 0) return FA_ERR_SHAPE;
+  if (page_size < 1 || page_size > kMaxPageSize || (page_size & (page_size - 1)) != 0) return FA_ERR_SHAPE;
+  if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (!scale_ok(scale) || num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_ARG;
+  // key positions (up to max_pages * page_size) stay below 2^30, so 32-bit key arithmetic
+  // cannot overflow; pool rows and table offsets are formed in 64 bits
+  if ((long long)max_pages * page_size > (1LL << 30) || (long long)num_pages * page_size > 0x7fffffffLL)
+    return FA_ERR_SHAPE;
+  if (!fits(1, (long long)num_pages * page_size, H, d)) return FA_ERR_SHAPE;
+  if (B == 0) return FA_OK;
+  if (!q || !k_pages || !v_pages || !block_table || !seqlens || !o) return FA_ERR_NULL;
+  if (!workspace || workspace_bytes < fa_decode_workspace_bytes(B, H, d, num_splits)) return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(workspace) ||
+      ((uintptr_t)block_table & 3u) != 0 || ((uintptr_t)seqlens & 3u) != 0)
+    return FA_ERR_ARG;
+  fa::DecodeArgs a{q, k_pages, v_pages, o, lse, (float*)workspace, B, H, 0, d, num_splits, scale,
+                   block_table, seqlens, page_size, num_pages, max_pages};
   return from_hip(fa::launch_decode_bf16(a, (hipStream_t)stream));
 }
 

@@ -10,6 +10,14 @@
 // non-temporal loads, eight keys in flight per lane.
 // Kernel 2 (combine): per (batch, head), weights chunk c by exp(m_c - M) (its softmax
 // mass relative to the largest), O = sum_c w_c o~_c / sum_c w_c l_c, LSE = M + ln sum.
+//
+// Paged caches ("Paged KV caches, a preview of serving"): the same kernels, except that
+// key n of sequence b is read from page block_table[b][n / page_size], slot
+// n % page_size, of a page pool. Each sequence has its own length and is cut into
+// num_splits chunks of ceil(L_b / num_splits) keys. The page ids of a window of up to
+// 256 pages are staged in LDS, so a key's address costs an LDS read; every page is still
+// read as whole, coalesced [H, d] rows. Table entries and lengths are clamped to the pool
+// and the table, so no input can send a read outside the buffers.
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -28,7 +36,13 @@ struct SplitArgs {
   float* part_o;
   int heads, cache_len, num_splits, chunk;
   float scale_log2;
+  // paged cache only
+  const int* block_table;
+  const int* seqlens;
+  int page_shift, num_pages, max_pages;
 };
+
+constexpr int kPageWindow = 256;  // page ids staged in LDS at a time
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -45,15 +59,24 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs p) {
   constexpr int CH = D / 8;             // lanes per key
   constexpr int KPP = kThreads / CH;    // keys per pass over the workgroup
   const int h = group_id_x() % p.heads;
   const int c = (group_id_x() / p.heads) % p.num_splits;
   const int b = group_id_x() / (p.heads * p.num_splits);
-  const int kbeg = c * p.chunk;
-  const int kend = min(kbeg + p.chunk, p.cache_len);
+  int kbeg, kend;
+  if constexpr (PAGED) {
+    const int cap = p.max_pages << p.page_shift;
+    const int len = min(max(p.seqlens[b], 0), cap);
+    const int chunk = (len + p.num_splits - 1) / p.num_splits;
+    kbeg = min(c * chunk, len);
+    kend = min(kbeg + chunk, len);
+  } else {
+    kbeg = c * p.chunk;
+    kend = min(kbeg + p.chunk, p.cache_len);
+  }
   const int tid = thread_id_x();
   const int sub = tid % CH, grp = tid / CH;
 
@@ -67,7 +90,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs p) {
     }
   }
   const size_t rs = (size_t)p.heads * D;
-  const size_t off = ((size_t)b * p.cache_len * p.heads + h) * D + sub * 8;
+  // contiguous: row n of sequence b; paged: row page*page_size + slot of the pool
+  const size_t off = PAGED ? (size_t)h * D + sub * 8 : ((size_t)b * p.cache_len * p.heads + h) * D + sub * 8;
   const uint16_t* __restrict__ kg = p.k + off;
   const uint16_t* __restrict__ vg = p.v + off;
 
@@ -75,15 +99,31 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs p) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = 0.f;
 
-  for (int n0 = kbeg; n0 < kend; n0 += KPP * kBatchKeys) {
+  __shared__ int sm_page[PAGED ? kPageWindow : 1];
+  const int wkeys = PAGED ? (kPageWindow << p.page_shift) : 0;
+  for (int wbeg = kbeg, wend; wbeg < kend; wbeg = wend) {
+  wend = PAGED && kend - wbeg > wkeys ? wbeg + wkeys : kend;
+  int p0 = 0;
+  if constexpr (PAGED) {
+    // stage the page ids of keys wbeg .. wend-1 (clamped into the pool)
+    p0 = wbeg >> p.page_shift;
+    const int np = ((wend - 1) >> p.page_shift) - p0 + 1;
+    __syncthreads();
+    if (tid < np) sm_page[tid] = min(max(p.block_table[(size_t)b * p.max_pages + p0 + tid], 0), p.num_pages - 1);
+    __syncthreads();
+  }
+  for (int n0 = wbeg; n0 < wend; n0 += KPP * kBatchKeys) {
     u32x4 kx[kBatchKeys], vx[kBatchKeys];
 #pragma unroll
     for (int i = 0; i < kBatchKeys; ++i) {
       const int n = n0 + i * KPP + grp;
       u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
-      if (n < kend) {
-        zk = __builtin_nontemporal_load((const u32x4*)(kg + (size_t)n * rs));
-        zv = __builtin_nontemporal_load((const u32x4*)(vg + (size_t)n * rs));
+      if (n < wend) {
+        size_t row = (size_t)n;
+        if constexpr (PAGED)
+          row = ((size_t)sm_page[(n >> p.page_shift) - p0] << p.page_shift) + (n & ((1 << p.page_shift) - 1));
+        zk = __builtin_nontemporal_load((const u32x4*)(kg + row * rs));
+        zv = __builtin_nontemporal_load((const u32x4*)(vg + row * rs));
       }
       kx[i] = zk;
       vx[i] = zv;
@@ -100,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs p) {
       }
       acc = group_sum<CH>(acc);
       const int n = n0 + i * KPP + grp;
-      s[i] = n < kend ? acc : -INFINITY;
+      s[i] = n < wend ? acc : -INFINITY;
       mb = fmaxf(mb, s[i]);
     }
     const float m_new = fmaxf(m, mb);
@@ -119,6 +159,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs p) {
       }
     }
     m = m_new;
+  }
   }
 
   // merge the KPP key groups of the workgroup
@@ -197,9 +238,18 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   s.num_splits = a.num_splits;
   s.chunk = (a.cache_len + a.num_splits - 1) / a.num_splits;
   s.scale_log2 = a.scale * kLog2e;
+  s.block_table = a.block_table;
+  s.seqlens = a.seqlens;
+  s.page_shift = 0;
+  while ((1 << s.page_shift) < a.page_size) ++s.page_shift;
+  s.num_pages = a.num_pages;
+  s.max_pages = a.max_pages;
   const size_t blocks = nbh * a.num_splits;
   if (blocks > 0x7fffffffu || nbh > 0x7fffffffu) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, s);
+  if (a.block_table)
+    hipLaunchKernelGGL((decode_split_kernel<D, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, s);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<D, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   CombineArgs c;

@@ -52,6 +52,11 @@ struct DecodeArgs {
   float* partials;  // workspace: [B, H, S] max, [B, H, S] sum, [B, H, S, d] output
   int batch, heads, cache_len, head_dim, num_splits;
   float scale;
+  // paged cache (block_table != NULL): caches are page pools [num_pages, page_size, H, d],
+  // block_table [B, max_pages] int32, seqlens [B] int32 (cache_len unused)
+  const int* block_table;
+  const int* seqlens;
+  int page_size, num_pages, max_pages;
 };
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);

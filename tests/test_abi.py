@@ -136,6 +136,34 @@ def test_decode_rejects(kw, code):
     assert decode(**kw) == code
 
 
+def decode_paged(**kw):
+    a = dict(q=FAKE, kp=FAKE, vp=FAKE, table=FAKE, seqlens=FAKE, o=FAKE, lse=None, B=2, H=4, d=128,
+             page_size=16, num_pages=100, max_pages=20, scale=0.1, splits=8, dtype=_clib.FA_DTYPE_BF16,
+             ws=FAKE, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return _clib.lib().fa_decode_paged(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(page_size=0), _clib.FA_ERR_SHAPE), (dict(page_size=24), _clib.FA_ERR_SHAPE),
+    (dict(page_size=2048), _clib.FA_ERR_SHAPE), (dict(num_pages=0), _clib.FA_ERR_SHAPE),
+    (dict(max_pages=0), _clib.FA_ERR_SHAPE), (dict(max_pages=(1 << 26) + 1), _clib.FA_ERR_SHAPE),
+    (dict(B=-1), _clib.FA_ERR_SHAPE), (dict(splits=0), _clib.FA_ERR_ARG),
+    (dict(ws_bytes=2 * 4 * 8 * 130 * 4 - 1), _clib.FA_ERR_WORKSPACE), (dict(ws=None), _clib.FA_ERR_WORKSPACE),
+    (dict(dtype=_clib.FA_DTYPE_F32), _clib.FA_ERR_DTYPE), (dict(table=None), _clib.FA_ERR_NULL),
+    (dict(seqlens=None), _clib.FA_ERR_NULL), (dict(d=96), _clib.FA_ERR_HEADDIM),
+    (dict(table=FAKE + 2), _clib.FA_ERR_ARG), (dict(vp=FAKE + 8), _clib.FA_ERR_ARG),
+    (dict(scale=-1.0), _clib.FA_ERR_ARG),
+])
+def test_decode_paged_rejects(kw, code):
+    assert decode_paged(**kw) == code
+
+
+def test_decode_paged_empty_batch_is_a_no_op():
+    # B = 0 returns before touching any pointer
+    assert decode_paged(B=0, q=None, kp=None, vp=None, table=None, seqlens=None, o=None, ws=None) == _clib.FA_OK
+
+
 def test_python_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     import io_aware_softmax_03_amd as fa
