@@ -21,6 +21,11 @@ Readings taken where the pages are silent (each is listed in the design notes):
   section describes). For the square shapes used here top-left and
   bottom-right coincide.
 * a row with every key masked has O = 0 and LSE = -inf.
+* grouped-query attention ("FlashAttention-2 and -3", "Using it, the real way":
+  fewer key-value heads than query heads, shared in groups without copying K
+  and V): with H query heads and Hkv key-value heads, the query heads form Hkv
+  consecutive groups of H / Hkv and group j reads key-value head j. Hkv = H is
+  ordinary multi-head attention.
 * the backward pass is the exact gradient of O(q, k, v) for an upstream dO,
   derived by calculus from the definition above; the pages state only that it
   recomputes the tiles from the saved LSE.
@@ -37,6 +42,14 @@ def _f64(x) -> np.ndarray:
 def _causal_keep(nq: int, nk: int) -> np.ndarray:
     """Boolean [nq, nk] mask: key j is visible to query i when j <= i (top-left)."""
     return np.arange(nk)[None, :] <= np.arange(nq)[:, None]
+
+
+def kv_head(h: int, H: int, Hkv: int) -> int:
+    """Key-value head read by query head h: query heads come in Hkv consecutive groups of
+    H / Hkv, group j sharing key-value head j (grouped-query attention)."""
+    if Hkv <= 0 or H % Hkv != 0:
+        raise ValueError(f"{H} query heads cannot be grouped over {Hkv} key-value heads")
+    return h // (H // Hkv)
 
 
 def attention_head(q, k, v, scale, causal=False, return_p=False):
@@ -59,14 +72,17 @@ def attention_head(q, k, v, scale, causal=False, return_p=False):
 
 
 def attn_fwd(q, k, v, scale, causal=False):
-    """Dense forward. q, k, v: [B, N, H, d]. Returns O [B, N, H, d], LSE [B, H, N]."""
+    """Dense forward. q: [B, N, H, d]; k, v: [B, N, Hkv, d] (Hkv divides H; Hkv = H for
+    multi-head attention). Returns O [B, N, H, d], LSE [B, H, N]."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, N, H, _ = q.shape
+    Hkv = k.shape[2]
     O = np.empty(q.shape[:3] + (v.shape[3],))
     lse = np.empty((B, H, N))
     for b in range(B):
         for h in range(H):
-            O[b, :, h, :], lse[b, h, :] = attention_head(q[b, :, h], k[b, :, h], v[b, :, h],
+            j = kv_head(h, H, Hkv)
+            O[b, :, h, :], lse[b, h, :] = attention_head(q[b, :, h], k[b, :, j], v[b, :, j],
                                                          scale, causal)
     return O, lse
 
@@ -74,7 +90,8 @@ def attn_fwd(q, k, v, scale, causal=False):
 def attn_fwd_varlen(q, k, v, cu_seqlens, scale, causal=False):
     """Packed variable-length forward ("Variable-length batches without padding").
 
-    q, k, v: [total_tokens, H, d]; sequence s occupies rows cu_seqlens[s] to
+    q: [total_tokens, H, d], k, v: [total_tokens, Hkv, d] (grouped as in attn_fwd);
+    sequence s occupies rows cu_seqlens[s] to
     cu_seqlens[s+1]. Attention never crosses a sequence boundary (block-diagonal
     document mask); causal is counted within each sequence.
     Returns O [total_tokens, H, d] and LSE [H, total_tokens].
@@ -84,6 +101,7 @@ def attn_fwd_varlen(q, k, v, cu_seqlens, scale, causal=False):
     if cu.ndim != 1 or cu[0] != 0 or np.any(np.diff(cu) < 0) or cu[-1] != q.shape[0]:
         raise ValueError("cu_seqlens must start at 0, be nondecreasing and end at total_tokens")
     T, H, _ = q.shape
+    Hkv = k.shape[1]
     O = np.zeros((T, H, v.shape[2]))
     lse = np.full((H, T), -np.inf)
     for s in range(len(cu) - 1):
@@ -91,7 +109,8 @@ def attn_fwd_varlen(q, k, v, cu_seqlens, scale, causal=False):
         if e == a:
             continue
         for h in range(H):
-            O[a:e, h, :], lse[h, a:e] = attention_head(q[a:e, h], k[a:e, h], v[a:e, h],
+            j = kv_head(h, H, Hkv)
+            O[a:e, h, :], lse[h, a:e] = attention_head(q[a:e, h], k[a:e, j], v[a:e, j],
                                                        scale, causal)
     return O, lse
 
@@ -123,6 +142,8 @@ def attn_bwd(q, k, v, do, scale, causal=False):
     """Dense backward. All tensors [B, N, H, d]; returns (dq, dk, dv) in float64."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     B, N, H, _ = q.shape
+    if k.shape[2] != H:
+        raise ValueError("the backward is defined here for multi-head attention only (Hkv = H)")
     dq, dk, dv = np.empty(q.shape), np.empty(k.shape), np.empty(v.shape)
     for b in range(B):
         for h in range(H):
@@ -143,14 +164,17 @@ def attn_decode_slice(q_vec, k_rows, v_rows, scale):
 
 
 def attn_decode(q, k_cache, v_cache, scale):
-    """Decode for a batch. q [B, H, d]; caches [B, L, H, d]. Returns O [B, H, d], LSE [B, H]."""
+    """Decode for a batch. q [B, H, d]; caches [B, L, Hkv, d] (grouped as in attn_fwd).
+    Returns O [B, H, d], LSE [B, H]."""
     q, kc, vc = _f64(q), _f64(k_cache), _f64(v_cache)
     B, H, _ = q.shape
+    Hkv = kc.shape[2]
     O = np.empty((B, H, vc.shape[3]))
     lse = np.empty((B, H))
     for b in range(B):
         for h in range(H):
-            O[b, h], lse[b, h] = attn_decode_slice(q[b, h], kc[b, :, h], vc[b, :, h], scale)
+            j = kv_head(h, H, Hkv)
+            O[b, h], lse[b, h] = attn_decode_slice(q[b, h], kc[b, :, j], vc[b, :, j], scale)
     return O, lse
 
 
@@ -161,10 +185,12 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, seqlens, scale):
     physical pages. Token t of sequence b is page block_table[b, t // P], slot t % P.
     Exactly seqlens[b] tokens are gathered (the slots past the end of the last page are not
     part of the sequence), then the contiguous decode runs. An empty sequence gives O = 0,
-    LSE = -inf (a row with no visible key). q [B, H, d]; returns O [B, H, d], LSE [B, H]."""
+    LSE = -inf (a row with no visible key). q [B, H, d]; pages [num_pages, P, Hkv, d]
+    (grouped as in attn_fwd); returns O [B, H, d], LSE [B, H]."""
     q, kp, vp = _f64(q), _f64(k_pages), _f64(v_pages)
     P = kp.shape[1]
     B, H, _ = q.shape
+    Hkv = kp.shape[2]
     O = np.zeros((B, H, vp.shape[3]))
     lse = np.full((B, H), -np.inf)
     for b in range(B):
@@ -175,5 +201,6 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, seqlens, scale):
         pg, slot = block_table[b, t // P], t % P
         k_rows, v_rows = kp[pg, slot], vp[pg, slot]  # [L, H, d]
         for h in range(H):
-            O[b, h], lse[b, h] = attn_decode_slice(q[b, h], k_rows[:, h], v_rows[:, h], scale)
+            j = kv_head(h, H, Hkv)
+            O[b, h], lse[b, h] = attn_decode_slice(q[b, h], k_rows[:, j], v_rows[:, j], scale)
     return O, lse
