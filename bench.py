@@ -7,7 +7,8 @@ convention 4*B*H*N^2*d/2 and as a fraction of the dense bf16 MFMA peak.
 
 Also measured in the same run (field "extra"): the backward (B=4, H=16, N=4096, d=128,
 causal), split-KV decode (B=64, H=32, L=32768, d=128, 64 splits), the same decode over a
-paged cache (16-token pages, lengths 16384..32768), the packed varlen
+paged cache (16-token pages, lengths 16384..32768), grouped-query decode (32 query heads
+over 8 key-value heads), the packed varlen
 forward (16 sequences, H=32, d=64) and the fp32 forward (N=256, d=64); and the float64
 CPU oracle timed on a bounded sample of the headline workload (field "cpu_baseline").
 
@@ -189,6 +190,24 @@ def extra_measurements(steps):
     out["decode_b64_h32_l32768_d128_s64"] = {"ms": round(ev, 4), "gbs": round(nb / ev / 1e6, 1),
                                              "frac_hbm_peak": round(nb / ev / 1e6 / PEAK_HBM_GBS, 4),
                                              "bytes_convention": "K and V caches read once + q + o"}
+    del q, kc, vc, ws
+    torch.cuda.empty_cache()
+
+    # grouped-query decode: 32 query heads over 8 key-value heads, otherwise as above
+    B, H, Hkv, L, d = 64, 32, 8, 32768, 128
+    gen.manual_seed(9)
+    q = torch.randn((B, H, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+    kc = torch.randn((B, L, Hkv, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+    vc = torch.randn((B, L, Hkv, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+    ws = torch.empty(fa.lib().fa_decode_workspace_bytes(B, H, d, 64), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    wall, ev, best = time_launches(lambda: fa.decode(q, kc, vc, num_splits=64, workspace=ws, out=(o, lse)),
+                                   max(3, steps // 2), 2)
+    nb = costs.decode_bytes(B, Hkv, L, d) + 2.0 * B * (H - Hkv) * d * 2
+    out["decode_gqa_b64_h32_kv8_l32768_d128_s64"] = {
+        "ms": round(ev, 4), "gbs": round(nb / ev / 1e6, 1), "frac_hbm_peak": round(nb / ev / 1e6 / PEAK_HBM_GBS, 4),
+        "bytes_convention": "K and V caches (8 heads) read once + q + o (32 heads)"}
     del q, kc, vc, ws
     torch.cuda.empty_cache()
 

@@ -19,6 +19,13 @@
  *            Attention and the Online-Softmax Trick" §7). Packed variable-length
  *            tensors are [total_tokens, H, d]. LSE is fp32 [B, H, N]
  *            ([H, total_tokens] for varlen, [B, H] for decode).
+ *   Heads    the forward and decode calls take Hkv key-value heads for H query
+ *            heads, Hkv dividing H (grouped-query attention: "FlashAttention-2
+ *            and -3", section "Using it, the real way", fewer key-value heads
+ *            shared in groups without copying K and V). Query heads form Hkv
+ *            consecutive groups of H / Hkv; group j reads key-value head j. K
+ *            and V then have Hkv in place of H in their shapes. Hkv = H is
+ *            ordinary multi-head attention; fa_bwd is multi-head only.
  *   Causal   query i sees key j when j <= i, both counted from the start of
  *            the sequence. For the square shapes accepted here this is both the
  *            top-left and the bottom-right alignment described in
@@ -69,7 +76,8 @@ const char* fa_strerror(int status);
 
 /*
  * fa_fwd — dense forward.
- *   q, k, v  [B, N, H, d] of `dtype` (read only)
+ *   q        [B, N, H, d] of `dtype` (read only)
+ *   k, v     [B, N, Hkv, d] of `dtype` (read only)
  *   o        [B, N, H, d] of `dtype` (written)
  *   lse      fp32 [B, H, N] (written): LSE_i = m_i + ln l_i, kept for fa_bwd
  *            ("Fewer non-matmul FLOPs"). May not be NULL.
@@ -80,12 +88,13 @@ const char* fa_strerror(int status);
  * sequence").
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-           int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
+           int B, int H, int Hkv, int N, int d, float scale, int causal, int dtype, void* stream);
 
 /*
  * fa_fwd_varlen — forward over sequences packed end to end without padding
  * ("FlashAttention-2 and -3", section "Variable-length batches without padding").
- *   q, k, v, o   [total_tokens, H, d]
+ *   q, o         [total_tokens, H, d]
+ *   k, v         [total_tokens, Hkv, d]
  *   lse          fp32 [H, total_tokens]
  *   cu_seqlens   device int32 [num_seqs + 1]: cu_seqlens[0] = 0, nondecreasing,
  *                cu_seqlens[num_seqs] = total_tokens. Sequence s occupies rows
@@ -99,7 +108,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  */
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                   const int* cu_seqlens, int num_seqs, int total_tokens, int max_seqlen,
-                  int H, int d, float scale, int causal, int dtype, void* stream);
+                  int H, int Hkv, int d, float scale, int causal, int dtype, void* stream);
 
 /* Bytes of workspace fa_bwd needs: the row statistic D = rowsum(dO * O) and the LSE in base 2
  * (LSE * log2(e)), each fp32 [B, H, N]. */
@@ -135,7 +144,7 @@ size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits);
  * "Decoding needs a different split").
  *   q          [B, H, d]
  *   k_cache,
- *   v_cache    [B, L, H, d]
+ *   v_cache    [B, L, Hkv, d]
  *   o          [B, H, d] (written)
  *   lse        fp32 [B, H] (written) or NULL
  *   num_splits 1 .. 1024 chunks of ceil(L / num_splits) keys. Each chunk yields
@@ -144,9 +153,11 @@ size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits);
  *              softmax mass). The merged result does not depend on num_splits
  *              beyond rounding.
  * The new token sees every cached key (no mask). Only FA_DTYPE_BF16.
+ * With Hkv < H one workgroup serves all query heads of a key-value head, so
+ * each cached key and value is read from memory once for the whole group.
  */
 int fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
-              int B, int H, int L, int d, float scale, int num_splits, int dtype,
+              int B, int H, int Hkv, int L, int d, float scale, int num_splits, int dtype,
               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -159,7 +170,7 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, 
  * ceil(seqlens[b] / num_splits) keys.
  *   q           [B, H, d]
  *   k_pages,
- *   v_pages     [num_pages, page_size, H, d]
+ *   v_pages     [num_pages, page_size, Hkv, d]
  *   block_table int32 [B, max_pages], row-major; entry j of row b is the page
  *               holding tokens j*page_size .. of sequence b. Entries past the
  *               sequence's last page are never read.
@@ -177,7 +188,7 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, 
  */
 int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
                     const int* block_table, const int* seqlens, void* o, float* lse,
-                    int B, int H, int d, int page_size, int num_pages, int max_pages,
+                    int B, int H, int Hkv, int d, int page_size, int num_pages, int max_pages,
                     float scale, int num_splits, int dtype,
                     void* workspace, size_t workspace_bytes, void* stream);
 

@@ -5,13 +5,15 @@ arguments (device pointers, sizes, the current HIP stream); every step of the
 computation runs in the HIP kernels of ``libfa.so``. PyTorch provides device
 memory and streams. Tensors must be contiguous device tensors:
 
-    fwd(q, k, v, scale=None, causal=False) -> (o, lse)          q,k,v [B, N, H, d]
-    fwd_varlen(q, k, v, cu_seqlens, max_seqlen, ...) -> (o, lse) q,k,v [T, H, d]
+    fwd(q, k, v, scale=None, causal=False) -> (o, lse)          q [B, N, H, d], k,v [B, N, Hkv, d]
+    fwd_varlen(q, k, v, cu_seqlens, max_seqlen, ...) -> (o, lse) q [T, H, d], k,v [T, Hkv, d]
     bwd(q, k, v, o, lse, do, scale=None, causal=False) -> (dq, dk, dv)   fp32 grads
     decode(q, k_cache, v_cache, scale=None, num_splits=64) -> (o, lse)   q [B, H, d]
     decode_paged(q, k_pages, v_pages, block_table, seqlens, ...) -> (o, lse)
 
-``scale`` defaults to 1/sqrt(d).
+``scale`` defaults to 1/sqrt(d). K and V may have fewer heads than Q (Hkv dividing H,
+grouped-query attention: query head h reads key-value head h // (H // Hkv)); the number
+is taken from their shapes. The backward is multi-head only.
 """
 from __future__ import annotations
 
@@ -60,11 +62,12 @@ def fwd(q, k, v, scale=None, causal=False, out=None):
     ``out=(o, lse)`` writes into preallocated tensors of those shapes."""
     torch = _torch()
     _require((q, k, v), ("q", "k", "v"))
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must all be [B, N, H, d]")
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
+        raise ValueError("q must be [B, N, H, d] and k, v [B, N, Hkv, d]")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share a dtype")
     B, N, H, d = q.shape
+    Hkv = k.shape[2]
     if out is None:
         o = torch.empty_like(q)
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
@@ -74,26 +77,28 @@ def fwd(q, k, v, scale=None, causal=False, out=None):
         if o.shape != q.shape or o.dtype != q.dtype or lse.shape != (B, H, N) or lse.dtype != torch.float32:
             raise ValueError("out must be (o [B, N, H, d] like q, lse fp32 [B, H, N])")
     st = lib().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                      B, H, N, d, _scale(scale, d), int(bool(causal)), _dtype_code(q), _stream(q.device))
+                      B, H, Hkv, N, d, _scale(scale, d), int(bool(causal)), _dtype_code(q), _stream(q.device))
     check(st, "fa_fwd")
     return o, lse
 
 
 def fwd_varlen(q, k, v, cu_seqlens, max_seqlen, scale=None, causal=False):
-    """Packed forward over sequences laid end to end. q, k, v: [T, H, d]; cu_seqlens: int32
+    """Packed forward over sequences laid end to end. q: [T, H, d], k, v: [T, Hkv, d]; cu_seqlens: int32
     device tensor [num_seqs + 1]; max_seqlen: the longest sequence length (host int).
     Returns O [T, H, d] and fp32 LSE [H, T]."""
     torch = _torch()
     _require((q, k, v, cu_seqlens), ("q", "k", "v", "cu_seqlens"))
-    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must all be [total_tokens, H, d]")
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or k.shape[0] != q.shape[0] or k.shape[2] != q.shape[2]:
+        raise ValueError("q must be [total_tokens, H, d] and k, v [total_tokens, Hkv, d]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
         raise TypeError("cu_seqlens must be a 1-D int32 tensor")
     T, H, d = q.shape
     o = torch.empty_like(q)
     lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
     st = lib().fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                             cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, T, int(max_seqlen), H, d,
+                             cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, T, int(max_seqlen), H, k.shape[1], d,
                              _scale(scale, d), int(bool(causal)), _dtype_code(q), _stream(q.device))
     check(st, "fa_fwd_varlen")
     return o, lse
@@ -132,13 +137,15 @@ def bwd(q, k, v, o, lse, do, scale=None, causal=False, out=None, workspace=None)
 
 
 def decode(q, k_cache, v_cache, scale=None, num_splits=64, workspace=None, out=None):
-    """Single-token decode. q [B, H, d]; caches [B, L, H, d]. Returns O [B, H, d], LSE [B, H]."""
+    """Single-token decode. q [B, H, d]; caches [B, L, Hkv, d]. Returns O [B, H, d], LSE [B, H]."""
     torch = _torch()
     _require((q, k_cache, v_cache), ("q", "k_cache", "v_cache"))
     B, H, d = q.shape
-    L = k_cache.shape[1]
-    if k_cache.shape != (B, L, H, d) or v_cache.shape != k_cache.shape:
-        raise ValueError("caches must be [B, L, H, d] matching q")
+    if k_cache.dim() != 4:
+        raise ValueError("caches must be [B, L, Hkv, d]")
+    L, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape != (B, L, Hkv, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [B, L, Hkv, d] matching q")
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise TypeError("q and the caches must share a dtype")
     if out is None:
@@ -153,21 +160,23 @@ def decode(q, k_cache, v_cache, scale=None, num_splits=64, workspace=None, out=N
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     st = lib().fa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                         B, H, L, d, _scale(scale, d), num_splits, _dtype_code(q),
+                         B, H, Hkv, L, d, _scale(scale, d), num_splits, _dtype_code(q),
                          workspace.data_ptr(), workspace.numel(), _stream(q.device))
     check(st, "fa_decode")
     return o, lse
 
 
 def decode_paged(q, k_pages, v_pages, block_table, seqlens, scale=None, num_splits=64, workspace=None, out=None):
-    """Single-token decode over a paged cache. q [B, H, d]; pages [num_pages, page_size, H, d];
+    """Single-token decode over a paged cache. q [B, H, d]; pages [num_pages, page_size, Hkv, d];
     block_table int32 [B, max_pages]; seqlens int32 [B]. Returns O [B, H, d], LSE [B, H]."""
     torch = _torch()
     _require((q, k_pages, v_pages, block_table, seqlens), ("q", "k_pages", "v_pages", "block_table", "seqlens"))
     B, H, d = q.shape
-    num_pages, page_size = k_pages.shape[0], k_pages.shape[1]
-    if k_pages.shape != (num_pages, page_size, H, d) or v_pages.shape != k_pages.shape:
-        raise ValueError("pages must be [num_pages, page_size, H, d] matching q")
+    if k_pages.dim() != 4:
+        raise ValueError("pages must be [num_pages, page_size, Hkv, d]")
+    num_pages, page_size, Hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    if k_pages.shape != (num_pages, page_size, Hkv, d) or v_pages.shape != k_pages.shape:
+        raise ValueError("pages must be [num_pages, page_size, Hkv, d] matching q")
     if k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
         raise TypeError("q and the pages must share a dtype")
     if block_table.dtype != torch.int32 or seqlens.dtype != torch.int32:
@@ -187,7 +196,7 @@ def decode_paged(q, k_pages, v_pages, block_table, seqlens, scale=None, num_spli
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     st = lib().fa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
-                               seqlens.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, d, page_size, num_pages,
+                               seqlens.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Hkv, d, page_size, num_pages,
                                max_pages, _scale(scale, d), num_splits, _dtype_code(q),
                                workspace.data_ptr(), workspace.numel(), _stream(q.device))
     check(st, "fa_decode_paged")

@@ -14,6 +14,8 @@ constexpr int kMaxSplits = 1024;
 constexpr int kMaxPageSize = 1024;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+// grouped-query attention: Hkv key-value heads shared by groups of H / Hkv query heads
+bool heads_ok(int H, int Hkv) { return H > 0 && Hkv > 0 && Hkv <= H && H % Hkv == 0; }
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
 // Checked on the bit pattern: this file is built with NaNs assumed absent, which lets the
 // compiler drop floating-point NaN tests.
@@ -53,9 +55,9 @@ const char* fa_strerror(int status) {
   }
 }
 
-int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
            int d, float scale, int causal, int dtype, void* stream) {
-  if (B < 0 || N < 0 || H <= 0) return FA_ERR_SHAPE;
+  if (B < 0 || N < 0 || !heads_ok(H, Hkv)) return FA_ERR_SHAPE;
   if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32) return FA_ERR_DTYPE;
   if (!scale_ok(scale) || (causal != 0 && causal != 1)) return FA_ERR_ARG;
@@ -63,15 +65,15 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   if (B == 0 || N == 0) return FA_OK;
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ARG;
-  fa::FwdArgs a{q, k, v, o, lse, nullptr, B, H, N, N, d, scale, causal != 0};
+  fa::FwdArgs a{q, k, v, o, lse, nullptr, B, H, Hkv, N, N, d, scale, causal != 0};
   hipStream_t s = (hipStream_t)stream;
   return from_hip(dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(a, s) : fa::launch_fwd_f32(a, s));
 }
 
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens,
-                  int num_seqs, int total_tokens, int max_seqlen, int H, int d, float scale, int causal,
-                  int dtype, void* stream) {
-  if (num_seqs < 0 || total_tokens < 0 || max_seqlen < 0 || H <= 0) return FA_ERR_SHAPE;
+                  int num_seqs, int total_tokens, int max_seqlen, int H, int Hkv, int d, float scale,
+                  int causal, int dtype, void* stream) {
+  if (num_seqs < 0 || total_tokens < 0 || max_seqlen < 0 || !heads_ok(H, Hkv)) return FA_ERR_SHAPE;
   if (max_seqlen > total_tokens) return FA_ERR_SHAPE;
   if (total_tokens > 0 && (max_seqlen == 0 || num_seqs == 0)) return FA_ERR_SHAPE;
   if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
@@ -81,7 +83,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
   if (total_tokens == 0) return FA_OK;
   if (!q || !k || !v || !o || !lse || !cu_seqlens) return FA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ARG;
-  fa::FwdArgs a{q, k, v, o, lse, cu_seqlens, num_seqs, H, max_seqlen, total_tokens, d, scale, causal != 0};
+  fa::FwdArgs a{q, k, v, o, lse, cu_seqlens, num_seqs, H, Hkv, max_seqlen, total_tokens, d, scale, causal != 0};
   hipStream_t s = (hipStream_t)stream;
   return from_hip(dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(a, s) : fa::launch_fwd_f32(a, s));
 }
@@ -114,10 +116,10 @@ size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits) {
   return (size_t)B * H * num_splits * (d + 2) * sizeof(float);
 }
 
-int fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B, int H, int L,
-              int d, float scale, int num_splits, int dtype, void* workspace, size_t workspace_bytes,
-              void* stream) {
-  if (B < 0 || H <= 0 || L <= 0) return FA_ERR_SHAPE;
+int fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B, int H,
+              int Hkv, int L, int d, float scale, int num_splits, int dtype, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  if (B < 0 || L <= 0 || !heads_ok(H, Hkv)) return FA_ERR_SHAPE;
   if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
   if (dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
   if (!scale_ok(scale) || num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_ARG;
@@ -126,16 +128,16 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, 
   if (!q || !k_cache || !v_cache || !o) return FA_ERR_NULL;
   if (!workspace || workspace_bytes < fa_decode_workspace_bytes(B, H, d, num_splits)) return FA_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace)) return FA_ERR_ARG;
-  fa::DecodeArgs a{q, k_cache, v_cache, o, lse, (float*)workspace, B, H, L, d, num_splits, scale,
+  fa::DecodeArgs a{q, k_cache, v_cache, o, lse, (float*)workspace, B, H, Hkv, L, d, num_splits, scale,
                    nullptr, nullptr, 0, 0, 0};
   return from_hip(fa::launch_decode_bf16(a, (hipStream_t)stream));
 }
 
 int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int* block_table,
-                    const int* seqlens, void* o, float* lse, int B, int H, int d, int page_size,
+                    const int* seqlens, void* o, float* lse, int B, int H, int Hkv, int d, int page_size,
                     int num_pages, int max_pages, float scale, int num_splits, int dtype, void* workspace,
                     size_t workspace_bytes, void* stream) {
-  if (B < 0 || H <= 0 || num_pages <= 0 || max_pages <= 0) return FA_ERR_SHAPE;
+  if (B < 0 || num_pages <= 0 || max_pages <= 0 || !heads_ok(H, Hkv)) return FA_ERR_SHAPE;
   if (page_size < 1 || page_size > kMaxPageSize || (page_size & (page_size - 1)) != 0) return FA_ERR_SHAPE;
   if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
   if (dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
@@ -144,14 +146,14 @@ int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, con
   // cannot overflow; pool rows and table offsets are formed in 64 bits
   if ((long long)max_pages * page_size > (1LL << 30) || (long long)num_pages * page_size > 0x7fffffffLL)
     return FA_ERR_SHAPE;
-  if (!fits(1, (long long)num_pages * page_size, H, d)) return FA_ERR_SHAPE;
+  if (!fits(1, (long long)num_pages * page_size, Hkv, d) || !fits(B, H, d, 1)) return FA_ERR_SHAPE;
   if (B == 0) return FA_OK;
   if (!q || !k_pages || !v_pages || !block_table || !seqlens || !o) return FA_ERR_NULL;
   if (!workspace || workspace_bytes < fa_decode_workspace_bytes(B, H, d, num_splits)) return FA_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(workspace) ||
       ((uintptr_t)block_table & 3u) != 0 || ((uintptr_t)seqlens & 3u) != 0)
     return FA_ERR_ARG;
-  fa::DecodeArgs a{q, k_pages, v_pages, o, lse, (float*)workspace, B, H, 0, d, num_splits, scale,
+  fa::DecodeArgs a{q, k_pages, v_pages, o, lse, (float*)workspace, B, H, Hkv, 0, d, num_splits, scale,
                    block_table, seqlens, page_size, num_pages, max_pages};
   return from_hip(fa::launch_decode_bf16(a, (hipStream_t)stream));
 }

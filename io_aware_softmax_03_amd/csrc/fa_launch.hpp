@@ -15,6 +15,7 @@ struct FwdArgs {
   const int* cu_seqlens;  // NULL for the dense [B, N, H, d] layout
   int batch;              // dense: B; packed: number of sequences
   int heads;
+  int kv_heads;           // K and V heads; divides heads (query head h reads h / (heads / kv_heads))
   int seqlen;             // dense: N; packed: max_seqlen (sizes the grid)
   int total_rows;         // dense: N; packed: total_tokens (LSE row stride)
   int head_dim;
@@ -50,9 +51,9 @@ struct DecodeArgs {
   void* o;
   float* lse;       // may be NULL
   float* partials;  // workspace: [B, H, S] max, [B, H, S] sum, [B, H, S, d] output
-  int batch, heads, cache_len, head_dim, num_splits;
+  int batch, heads, kv_heads, cache_len, head_dim, num_splits;
   float scale;
-  // paged cache (block_table != NULL): caches are page pools [num_pages, page_size, H, d],
+  // paged cache (block_table != NULL): caches are page pools [num_pages, page_size, Hkv, d],
   // block_table [B, max_pages] int32, seqlens [B] int32 (cache_len unused)
   const int* block_table;
   const int* seqlens;

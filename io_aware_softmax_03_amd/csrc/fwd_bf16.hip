@@ -44,6 +44,8 @@ struct FwdKernelArgs {
   float* lse;
   const int* cu_seqlens;
   int heads;
+  int kv_heads;    // K and V heads; query head h reads kv head h / group
+  int group;       // heads / kv_heads
   int seqlen;      // dense sequence length (unused for packed)
   int total_rows;  // LSE row stride for packed, N for dense
   int nqb;         // workgroups per (sequence, head): query blocks, or pairs of them if causal
@@ -109,16 +111,26 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
   auto kbuf = [&](auto bc) -> char* { return (decltype(bc)::value & 1) ? k_lds1 : k_lds0; };
   auto vbuf = [&](auto bc) -> char* { return (decltype(bc)::value & 1) ? v_lds1 : v_lds0; };
 
-  // ---- work decode, XCD-aware: workgroup w runs on XCD w % 8. With a head count divisible by
-  // 8, XCD x takes heads x, x+8, ... of every sequence (all query blocks of a head share that
-  // XCD's L2 for K and V, and every XCD gets the same mix of sequence lengths); otherwise each
-  // XCD takes a contiguous range of (sequence*head, block). Causal: workgroup p of a sequence
+  // ---- work decode, XCD-aware: workgroup w runs on XCD w % 8. With a key-value head count
+  // divisible by 8, XCD x takes key-value heads x, x+8, ... of every sequence with every query
+  // head that reads them (all query blocks of those heads share that XCD's L2 for K and V,
+  // and every XCD gets the same mix of sequence lengths); else, with a query head count
+  // divisible by 8, query heads x, x+8, ...; otherwise each XCD takes a contiguous range of
+  // (sequence*head, block). Causal: workgroup p of a sequence
   // takes query blocks nb-1-p and p (nb blocks in the sequence), so all workgroups of a
   // sequence do the same number of key blocks; non-causal: one block each.
   const int total = p.grid;
   const int w = group_id_x();
   int pi, h, bs;
-  if (p.heads % 8 == 0) {
+  if (p.kv_heads % 8 == 0) {
+    const int slot = w / 8, hx = p.kv_heads / 8;
+    pi = slot % p.nqb;
+    int rest = slot / p.nqb;
+    const int j = rest % p.group;
+    rest /= p.group;
+    h = (w % 8 + 8 * (rest % hx)) * p.group + j;
+    bs = rest / hx;
+  } else if (p.heads % 8 == 0) {
     const int slot = w / 8, hx = p.heads / 8;
     pi = slot % p.nqb;
     const int rest = slot / p.nqb;
@@ -150,11 +162,13 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
     const int r = lane & 31;
     const int hh = lane >> 5;
     const int nh = r >> 4, gi = lane & 15;
-    const int rs = p.heads * D;  // row stride in elements (< 2^31 by the host checks)
+    const int rs = p.heads * D;     // Q / O row stride in elements (< 2^31 by the host checks)
+    const int rsk = p.kv_heads * D; // K / V row stride
     const size_t base = ((size_t)seq_start * p.heads + h) * D;
+    const size_t base_kv = ((size_t)seq_start * p.kv_heads + h / p.group) * D;
     const uint16_t* __restrict__ qg = p.q + base;
-    const uint16_t* __restrict__ kg = p.k + base;
-    const uint16_t* __restrict__ vg = p.v + base;
+    const uint16_t* __restrict__ kg = p.k + base_kv;
+    const uint16_t* __restrict__ vg = p.v + base_kv;
 
     const int qw = q0 + kQW * wid;  // first query row of this wave
     const bool wave_active = qw < L;
@@ -193,15 +207,15 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
     for (int it = 0; it < LOADS; ++it) {
       const int lrow = (wid * LOADS + it) * ROWS_PER_KB + lane / CH;
       const int phys = lane % CH;
-      k_src[it] = (unsigned)(lrow * rs + (phys ^ swz_k<D>(lrow)) * 8) * 2u;
-      v_src[it] = (unsigned)(lrow * rs + (phys ^ swz_v<D>(lrow)) * 8) * 2u;
+      k_src[it] = (unsigned)(lrow * rsk + (phys ^ swz_k<D>(lrow)) * 8) * 2u;
+      v_src[it] = (unsigned)(lrow * rsk + (phys ^ swz_v<D>(lrow)) * 8) * 2u;
     }
     // copy key block kt of K (IS_K) or V into buffer BUF
     auto issue = [&](auto is_kc, auto bufc, int kt) {
       constexpr bool IS_K = decltype(is_kc)::value;
       const int k0 = kt * kBC;
-      const unsigned bytes = (unsigned)(min(kBC - 1, L - 1 - k0) * rs + D) * 2u;
-      const __amdgpu_buffer_rsrc_t src = make_rsrc((IS_K ? kg : vg) + (size_t)k0 * rs, bytes);
+      const unsigned bytes = (unsigned)(min(kBC - 1, L - 1 - k0) * rsk + D) * 2u;
+      const __amdgpu_buffer_rsrc_t src = make_rsrc((IS_K ? kg : vg) + (size_t)k0 * rsk, bytes);
       char* dst = (IS_K ? kbuf(bufc) : vbuf(bufc)) + wid * LOADS * 1024;
 #pragma unroll
       for (int it = 0; it < LOADS; ++it) copy16_to_lds(src, IS_K ? k_src[it] : v_src[it], dst + it * 1024);
@@ -630,6 +644,8 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.lse = a.lse;
   p.cu_seqlens = a.cu_seqlens;
   p.heads = a.heads;
+  p.kv_heads = a.kv_heads;
+  p.group = a.heads / a.kv_heads;
   p.seqlen = a.seqlen;
   p.total_rows = a.total_rows;
   const int nqb = (a.seqlen + kBR - 1) / kBR;

@@ -22,7 +22,7 @@ struct F32Args {
   float* o;
   float* lse;
   const int* cu_seqlens;
-  int heads, seqlen, total_rows, nqb;
+  int heads, kv_heads, group, seqlen, total_rows, nqb;
   float scale_log2;
 };
 
@@ -47,8 +47,10 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args p) {
   }
   const int q0 = qb * RPB;
   if (q0 >= L) return;
-  const size_t rs = (size_t)p.heads * D;
+  const size_t rs = (size_t)p.heads * D;      // Q / O row stride
+  const size_t rsk = (size_t)p.kv_heads * D;  // K / V row stride
   const size_t base = ((size_t)seq_start * p.heads + h) * D;
+  const size_t base_kv = ((size_t)seq_start * p.kv_heads + h / p.group) * D;
   const int tid = thread_id_x();
   const int part = tid % TPR;
   const int myq = q0 + tid / TPR;
@@ -70,8 +72,8 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args p) {
       const int row = e / D, col = e % D;
       const int key = k0 + row;
       const bool in = key < L;
-      ks[e] = in ? p.k[base + (size_t)key * rs + col] : 0.f;
-      vs[e] = in ? p.v[base + (size_t)key * rs + col] : 0.f;
+      ks[e] = in ? p.k[base_kv + (size_t)key * rsk + col] : 0.f;
+      vs[e] = in ? p.v[base_kv + (size_t)key * rsk + col] : 0.f;
     }
     __syncthreads();
     float s[kKT];
@@ -130,6 +132,8 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.lse = a.lse;
   p.cu_seqlens = a.cu_seqlens;
   p.heads = a.heads;
+  p.kv_heads = a.kv_heads;
+  p.group = a.heads / a.kv_heads;
   p.seqlen = a.seqlen;
   p.total_rows = a.total_rows;
   p.nqb = (a.seqlen + RPB - 1) / RPB;

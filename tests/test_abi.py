@@ -57,7 +57,7 @@ FAKE = 0x10000  # a 16-byte aligned non-null address; never dereferenced by fail
 
 
 def fwd(**kw):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, N=16, d=64, scale=0.125,
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, Hkv=1, N=16, d=64, scale=0.125,
              causal=0, dtype=_clib.FA_DTYPE_BF16, stream=None)
     a.update(kw)
     return _clib.lib().fa_fwd(*a.values())
@@ -65,6 +65,8 @@ def fwd(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(B=-1), _clib.FA_ERR_SHAPE), (dict(H=0), _clib.FA_ERR_SHAPE), (dict(N=-5), _clib.FA_ERR_SHAPE),
+    (dict(Hkv=0), _clib.FA_ERR_SHAPE), (dict(Hkv=2), _clib.FA_ERR_SHAPE), (dict(H=6, Hkv=4), _clib.FA_ERR_SHAPE),
+    (dict(H=6, Hkv=-3), _clib.FA_ERR_SHAPE),
     (dict(d=96), _clib.FA_ERR_HEADDIM), (dict(d=256), _clib.FA_ERR_HEADDIM),
     (dict(dtype=7), _clib.FA_ERR_DTYPE), (dict(scale=0.0), _clib.FA_ERR_ARG),
     (dict(scale=float("nan")), _clib.FA_ERR_ARG), (dict(scale=-1.0), _clib.FA_ERR_ARG),
@@ -83,7 +85,7 @@ def test_fwd_empty_is_noop():
 
 def varlen(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, cu=FAKE, num_seqs=2, total=10, max_seqlen=6, H=2,
-             d=128, scale=0.1, causal=1, dtype=_clib.FA_DTYPE_BF16, stream=None)
+             Hkv=2, d=128, scale=0.1, causal=1, dtype=_clib.FA_DTYPE_BF16, stream=None)
     a.update(kw)
     return _clib.lib().fa_fwd_varlen(*a.values())
 
@@ -93,6 +95,7 @@ def varlen(**kw):
     (dict(max_seqlen=0), _clib.FA_ERR_SHAPE), (dict(num_seqs=0), _clib.FA_ERR_SHAPE),
     (dict(num_seqs=-1), _clib.FA_ERR_SHAPE), (dict(d=32), _clib.FA_ERR_HEADDIM),
     (dict(dtype=3), _clib.FA_ERR_DTYPE), (dict(causal=-1), _clib.FA_ERR_ARG),
+    (dict(Hkv=3), _clib.FA_ERR_SHAPE), (dict(Hkv=0), _clib.FA_ERR_SHAPE),
 ])
 def test_varlen_rejects(kw, code):
     assert varlen(**kw) == code
@@ -120,7 +123,7 @@ def test_bwd_rejects(kw, code):
 
 
 def decode(**kw):
-    a = dict(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, lse=None, B=2, H=4, L=1000, d=128, scale=0.1, splits=8,
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, lse=None, B=2, H=4, Hkv=4, L=1000, d=128, scale=0.1, splits=8,
              dtype=_clib.FA_DTYPE_BF16, ws=FAKE, ws_bytes=1 << 20, stream=None)
     a.update(kw)
     return _clib.lib().fa_decode(*a.values())
@@ -131,13 +134,14 @@ def decode(**kw):
     (dict(ws_bytes=2 * 4 * 8 * 130 * 4 - 1), _clib.FA_ERR_WORKSPACE), (dict(ws=None), _clib.FA_ERR_WORKSPACE),
     (dict(dtype=_clib.FA_DTYPE_F32), _clib.FA_ERR_DTYPE), (dict(kc=None), _clib.FA_ERR_NULL),
     (dict(d=100), _clib.FA_ERR_HEADDIM), (dict(ws=FAKE + 8), _clib.FA_ERR_ARG),
+    (dict(Hkv=3), _clib.FA_ERR_SHAPE), (dict(Hkv=8), _clib.FA_ERR_SHAPE), (dict(Hkv=0), _clib.FA_ERR_SHAPE),
 ])
 def test_decode_rejects(kw, code):
     assert decode(**kw) == code
 
 
 def decode_paged(**kw):
-    a = dict(q=FAKE, kp=FAKE, vp=FAKE, table=FAKE, seqlens=FAKE, o=FAKE, lse=None, B=2, H=4, d=128,
+    a = dict(q=FAKE, kp=FAKE, vp=FAKE, table=FAKE, seqlens=FAKE, o=FAKE, lse=None, B=2, H=4, Hkv=2, d=128,
              page_size=16, num_pages=100, max_pages=20, scale=0.1, splits=8, dtype=_clib.FA_DTYPE_BF16,
              ws=FAKE, ws_bytes=1 << 20, stream=None)
     a.update(kw)
@@ -153,7 +157,7 @@ def decode_paged(**kw):
     (dict(dtype=_clib.FA_DTYPE_F32), _clib.FA_ERR_DTYPE), (dict(table=None), _clib.FA_ERR_NULL),
     (dict(seqlens=None), _clib.FA_ERR_NULL), (dict(d=96), _clib.FA_ERR_HEADDIM),
     (dict(table=FAKE + 2), _clib.FA_ERR_ARG), (dict(vp=FAKE + 8), _clib.FA_ERR_ARG),
-    (dict(scale=-1.0), _clib.FA_ERR_ARG),
+    (dict(scale=-1.0), _clib.FA_ERR_ARG), (dict(Hkv=3), _clib.FA_ERR_SHAPE), (dict(Hkv=5), _clib.FA_ERR_SHAPE),
 ])
 def test_decode_paged_rejects(kw, code):
     assert decode_paged(**kw) == code
