@@ -100,3 +100,46 @@ def causal_tiles_visited(n_rows, n_cols, block_rows, block_cols):
         last_row = min((i + 1) * block_rows, n_rows) - 1
         count += min(math.ceil(n_cols / block_cols), last_row // block_cols + 1)
     return count
+
+
+def band_key_range(i, nq, nk, causal, window_left=-1, window_right=-1):
+    """Visible keys [lo, hi] (inclusive; empty when lo > hi) of query i under the
+    bottom-right alignment: query i stands at key position i + nk - nq; a sliding window
+    keeps `window_left` keys before and `window_right` after it (negative: unlimited;
+    causal: right = 0) ("Using it, the real way")."""
+    pos = i + nk - nq
+    right = 0 if causal else window_right
+    hi = nk - 1 if right < 0 else min(nk - 1, pos + right)
+    lo = 0 if window_left < 0 else max(0, pos - window_left)
+    return lo, hi
+
+
+def band_visible_pairs(nq, nk, causal, window_left=-1, window_right=-1):
+    """Number of visible (query, key) pairs: the useful score entries of one head."""
+    total = 0
+    for i in range(nq):
+        lo, hi = band_key_range(i, nq, nk, causal, window_left, window_right)
+        total += max(0, hi - lo + 1)
+    return total
+
+
+def band_fwd_flops(B, H, nq, nk, d, causal, window_left=-1, window_right=-1):
+    """Useful forward FLOPs of a banded forward: 4*d per visible pair (two products)."""
+    return 4.0 * B * H * d * band_visible_pairs(nq, nk, causal, window_left, window_right)
+
+
+def band_tiles_visited(nq, nk, block_q, block_k, causal, window_left=-1, window_right=-1):
+    """(query block, key block) tiles holding at least one visible entry: per query block,
+    the key blocks between its first row's lowest visible key and its last row's highest.
+    Tiles outside are skipped ("a block mask of the tiles that are entirely masked")."""
+    tiles = []
+    for qb in range(math.ceil(nq / block_q)):
+        first, last = qb * block_q, min((qb + 1) * block_q, nq) - 1
+        ranges = [band_key_range(i, nq, nk, causal, window_left, window_right) for i in range(first, last + 1)]
+        ranges = [(a, b) for a, b in ranges if a <= b]
+        if not ranges:
+            continue
+        # the rows' key ranges move right with the row, overlapping: their union is one range
+        lo, hi = min(a for a, _ in ranges), max(b for _, b in ranges)
+        tiles.extend((qb, kb) for kb in range(lo // block_k, hi // block_k + 1))
+    return tiles

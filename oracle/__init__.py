@@ -25,7 +25,7 @@ backward, and the figures the pages print (``tests/golden``). No function is
 "parity unpinned".
 """
 from .attention import (  # noqa: F401
-    kv_head, attention_head, attn_fwd, attn_fwd_varlen, attn_bwd_head, attn_bwd,
+    kv_head, band_keep, attention_head, attn_fwd, attn_fwd_window, attn_fwd_varlen, attn_bwd_head, attn_bwd,
     attn_decode, attn_decode_slice, attn_decode_paged,
 )
 from .algorithms import (  # noqa: F401

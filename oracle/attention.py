@@ -21,6 +21,14 @@ Readings taken where the pages are silent (each is listed in the design notes):
   section describes). For the square shapes used here top-left and
   bottom-right coincide.
 * a row with every key masked has O = 0 and LSE = -inf.
+* rectangular causal (Nq queries, Nk keys, Nq != Nk) is aligned bottom-right, the
+  flash-attn convention the same section recommends for chunked prefill and decoding
+  with a cache: query i stands at key position i + Nk - Nq and sees keys up to it. A
+  sliding window (the same section: kernels support sliding windows natively) follows
+  flash-attn's (left, right) form around that position: key j is visible when
+  i + Nk - Nq - left <= j <= i + Nk - Nq + right, a negative bound meaning none and
+  causal meaning right = 0. With a 64-token causal window each query sees itself and the
+  64 keys before it.
 * grouped-query attention ("FlashAttention-2 and -3", "Using it, the real way":
   fewer key-value heads than query heads, shared in groups without copying K
   and V): with H query heads and Hkv key-value heads, the query heads form Hkv
@@ -52,12 +60,30 @@ def kv_head(h: int, H: int, Hkv: int) -> int:
     return h // (H // Hkv)
 
 
-def attention_head(q, k, v, scale, causal=False, return_p=False):
-    """Forward attention for one (batch, head) slice; returns (O, LSE[, P])."""
+def band_keep(nq: int, nk: int, causal: bool, window_left: int = -1, window_right: int = -1) -> np.ndarray:
+    """Boolean [nq, nk] visibility with the bottom-right alignment: query i stands at key
+    position i + nk - nq; key j is visible when it lies within `window_left` keys before and
+    `window_right` keys after that position (a negative bound: unlimited; causal: right 0)."""
+    pos = np.arange(nq)[:, None] + (nk - nq)
+    j = np.arange(nk)[None, :]
+    keep = np.ones((nq, nk), dtype=bool)
+    right = 0 if causal else window_right
+    if right >= 0:
+        keep &= j <= pos + right
+    if window_left >= 0:
+        keep &= j >= pos - window_left
+    return keep
+
+
+def attention_head(q, k, v, scale, causal=False, return_p=False, keep=None):
+    """Forward attention for one (batch, head) slice; returns (O, LSE[, P]).
+    ``causal`` applies the top-left mask; ``keep`` (boolean [Nq, Nk]) any other."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     S = float(scale) * (q @ k.T)
     if causal:
         S = np.where(_causal_keep(q.shape[0], k.shape[0]), S, -np.inf)
+    if keep is not None:
+        S = np.where(keep, S, -np.inf)
     m = S.max(axis=1) if S.shape[1] else np.full(S.shape[0], -np.inf)
     has_key = np.isfinite(m)
     m_ref = np.where(has_key, m, 0.0)
@@ -84,6 +110,24 @@ def attn_fwd(q, k, v, scale, causal=False):
             j = kv_head(h, H, Hkv)
             O[b, :, h, :], lse[b, h, :] = attention_head(q[b, :, h], k[b, :, j], v[b, :, j],
                                                          scale, causal)
+    return O, lse
+
+
+def attn_fwd_window(q, k, v, scale, causal=False, window_left=-1, window_right=-1):
+    """Forward with Nq queries against Nk keys, bottom-right aligned, with an optional
+    sliding window (see band_keep). q: [B, Nq, H, d]; k, v: [B, Nk, Hkv, d].
+    Returns O [B, Nq, H, d], LSE [B, H, Nq]; a query with no visible key gets O = 0,
+    LSE = -inf."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Nq, H, _ = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    keep = band_keep(Nq, Nk, causal, window_left, window_right)
+    O = np.empty(q.shape[:3] + (v.shape[3],))
+    lse = np.empty((B, H, Nq))
+    for b in range(B):
+        for h in range(H):
+            j = kv_head(h, H, Hkv)
+            O[b, :, h, :], lse[b, h, :] = attention_head(q[b, :, h], k[b, :, j], v[b, :, j], scale, keep=keep)
     return O, lse
 
 
