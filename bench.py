@@ -8,7 +8,8 @@ convention 4*B*H*N^2*d/2 and as a fraction of the dense bf16 MFMA peak.
 Also measured in the same run (field "extra"): the backward (B=4, H=16, N=4096, d=128,
 causal), split-KV decode (B=64, H=32, L=32768, d=128, 64 splits), the same decode over a
 paged cache (16-token pages, lengths 16384..32768), grouped-query decode (32 query heads
-over 8 key-value heads), the packed varlen
+over 8 key-value heads), a chunked prefill (2048 queries on 16384 keys) and a 1024-key
+sliding window (N=8192) through the banded forward, the packed varlen
 forward (16 sequences, H=32, d=64) and the fp32 forward (N=256, d=64); and the float64
 CPU oracle timed on a bounded sample of the headline workload (field "cpu_baseline").
 
@@ -167,6 +168,25 @@ def extra_measurements(steps):
                                           "frac_mfma_peak": round(fl / ev / 1e9 / PEAK_BF16_TFLOPS, 4),
                                           "total_tokens": T}
     del q, k, v
+
+    # banded forwards (bf16, d=128, causal, bottom-right): chunked prefill of 2048 new
+    # queries against a 16384-key cache, and a 1024-key sliding window over 8192 tokens.
+    # Work counted as 4*d per visible (query, key) pair.
+    for name, B, H, Nq, Nk, left in (("fwd_chunked_prefill_b4_h16_q2048_k16384_d128", 4, 16, 2048, 16384, -1),
+                                     ("fwd_sliding_window1024_b2_h16_n8192_d128", 2, 16, 8192, 8192, 1024)):
+        d = 128
+        gen.manual_seed(10)
+        q = torch.randn((B, Nq, H, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+        k, v = (torch.randn((B, Nk, H, d), generator=gen, device="cuda", dtype=torch.bfloat16) for _ in range(2))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda")
+        wall, ev, best = time_launches(lambda: fa.fwd_window(q, k, v, causal=True, window=(left, -1), out=(o, lse)),
+                                       steps, 3)
+        fl = costs.band_fwd_flops(B, H, Nq, Nk, d, True, left)
+        out[name] = {"ms": round(ev, 4), "tflops": round(fl / ev / 1e9, 2),
+                     "frac_mfma_peak": round(fl / ev / 1e9 / PEAK_BF16_TFLOPS, 4),
+                     "flops_convention": "4*d per visible (query, key) pair"}
+        del q, k, v, o, lse
 
     # fp32 forward, B=1 H=1 N=256 d=64 (launch-latency bound)
     gen.manual_seed(1)

@@ -46,8 +46,8 @@
  *            never a fallback to another algorithm ("Using it, the real way":
  *            ask for the fused kernel and get an error rather than a slower
  *            path). A failed kernel launch returns FA_ERR_HIP.
- *   Sizes    element counts of every tensor must fit in int64; per-sequence
- *            lengths fit in int32.
+ *   Sizes    element counts of every tensor must fit in int64; sequence
+ *            lengths (and packed token counts) are at most 2^30.
  */
 #ifndef FA_H
 #define FA_H
@@ -89,6 +89,28 @@ const char* fa_strerror(int status);
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int Hkv, int N, int d, float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_fwd_window — forward with Nq queries against Nk keys and an optional
+ * sliding window ("FlashAttention-2 and -3", section "Using it, the real way":
+ * causal aligned bottom-right, as chunked prefill and decoding with a cache
+ * need; kernels support sliding windows natively; a block mask skips the tiles
+ * with no visible entry).
+ *   q, o          [B, Nq, H, d];  k, v  [B, Nk, Hkv, d];  lse  fp32 [B, H, Nq]
+ *   Query i stands at key position p_i = i + Nk - Nq. Key j is visible when
+ *     p_i - window_left <= j    (window_left >= 0; -1: no lower bound)
+ *     j <= p_i + window_right   (window_right >= 0; -1: no upper bound)
+ *   causal = 1 sets the upper bound to p_i (window_right must be -1 or 0). With
+ *   Nq = Nk, causal and no window this is fa_fwd's causal mask; a 64-key causal
+ *   window shows each query itself and the 64 keys before it.
+ *   A query with no visible key (e.g. i < Nq - Nk under causal) gets O = 0 and
+ *   LSE = -inf. Per 256-query block only the 32-key blocks between the first
+ *   row's lowest and the last row's highest visible key are read.
+ *   Nq, Nk <= 2^30; Nk may be 0 (every row then has no visible key).
+ */
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int Hkv, int Nq, int Nk, int d, float scale,
+                  int causal, int window_left, int window_right, int dtype, void* stream);
 
 /*
  * fa_fwd_varlen — forward over sequences packed end to end without padding

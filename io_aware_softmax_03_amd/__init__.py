@@ -6,6 +6,8 @@ computation runs in the HIP kernels of ``libfa.so``. PyTorch provides device
 memory and streams. Tensors must be contiguous device tensors:
 
     fwd(q, k, v, scale=None, causal=False) -> (o, lse)          q [B, N, H, d], k,v [B, N, Hkv, d]
+    fwd_window(q, k, v, scale=None, causal=False, window=(-1, -1)) -> (o, lse)
+                                                 q [B, Nq, H, d], k,v [B, Nk, Hkv, d]
     fwd_varlen(q, k, v, cu_seqlens, max_seqlen, ...) -> (o, lse) q [T, H, d], k,v [T, Hkv, d]
     bwd(q, k, v, o, lse, do, scale=None, causal=False) -> (dq, dk, dv)   fp32 grads
     decode(q, k_cache, v_cache, scale=None, num_splits=64) -> (o, lse)   q [B, H, d]
@@ -23,7 +25,7 @@ from ._clib import (  # noqa: F401
     FAError, FA_DTYPE_BF16, FA_DTYPE_F32, check, lib, strerror,
 )
 
-__all__ = ["fwd", "fwd_varlen", "bwd", "decode", "decode_paged", "FAError", "lib"]
+__all__ = ["fwd", "fwd_window", "fwd_varlen", "bwd", "decode", "decode_paged", "FAError", "lib"]
 
 
 def _torch():
@@ -79,6 +81,35 @@ def fwd(q, k, v, scale=None, causal=False, out=None):
     st = lib().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                       B, H, Hkv, N, d, _scale(scale, d), int(bool(causal)), _dtype_code(q), _stream(q.device))
     check(st, "fa_fwd")
+    return o, lse
+
+
+def fwd_window(q, k, v, scale=None, causal=False, window=(-1, -1), out=None):
+    """Forward with Nq queries against Nk keys, bottom-right aligned, and an optional
+    sliding window ``(left, right)`` around each query's key position i + Nk - Nq (-1: no
+    bound; causal fixes right = 0). q [B, Nq, H, d], k, v [B, Nk, Hkv, d].
+    Returns O [B, Nq, H, d] and fp32 LSE [B, H, Nq]."""
+    torch = _torch()
+    _require((q, k, v), ("q", "k", "v"))
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
+        raise ValueError("q must be [B, Nq, H, d] and k, v [B, Nk, Hkv, d]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    B, Nq, H, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    left, right = (int(w) for w in window)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        _require((o, lse), ("o", "lse"))
+        if o.shape != q.shape or o.dtype != q.dtype or lse.shape != (B, H, Nq) or lse.dtype != torch.float32:
+            raise ValueError("out must be (o [B, Nq, H, d] like q, lse fp32 [B, H, Nq])")
+    st = lib().fa_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                             B, H, Hkv, Nq, Nk, d, _scale(scale, d), int(bool(causal)), left, right,
+                             _dtype_code(q), _stream(q.device))
+    check(st, "fa_fwd_window")
     return o, lse
 
 

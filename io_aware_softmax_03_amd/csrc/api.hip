@@ -37,6 +37,41 @@ int fits(long long a, long long b, long long c, long long d) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+// longest query or key sequence the forward accepts: keeps every key position plus a mask
+// offset inside int32
+constexpr long long kMaxSeq = 1LL << 30;
+
+long long clamp_off(long long x) { return x < -kMaxSeq ? -kMaxSeq : (x > kMaxSeq ? kMaxSeq : x); }
+
+// Forward launch arguments. Masking is bottom-right aligned: query i sits at key position
+// i + nk - nq; a window keeps `left` keys before it and `right` after (-1: unlimited), and
+// causal means right = 0.
+fa::FwdArgs fwd_args(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu,
+                     int batch, int H, int Hkv, int nq, int total_rows, int nk, int d, float scale,
+                     bool causal, int left, int right) {
+  fa::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.cu_seqlens = cu;
+  a.batch = batch;
+  a.heads = H;
+  a.kv_heads = Hkv;
+  a.seqlen = nq;
+  a.total_rows = total_rows;
+  a.head_dim = d;
+  a.scale = scale;
+  a.seqlen_k = nk;
+  const long long off = (long long)nk - nq;
+  const int r = causal ? 0 : right;
+  a.banded = r >= 0;
+  a.hi_off = a.banded ? (int)clamp_off(off + r) : 0;
+  a.lo_off = left >= 0 ? (int)clamp_off(off - left) : fa::kNoLowerBound;
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -57,7 +92,7 @@ const char* fa_strerror(int status) {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
            int d, float scale, int causal, int dtype, void* stream) {
-  if (B < 0 || N < 0 || !heads_ok(H, Hkv)) return FA_ERR_SHAPE;
+  if (B < 0 || N < 0 || N > kMaxSeq || !heads_ok(H, Hkv)) return FA_ERR_SHAPE;
   if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32) return FA_ERR_DTYPE;
   if (!scale_ok(scale) || (causal != 0 && causal != 1)) return FA_ERR_ARG;
@@ -65,7 +100,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   if (B == 0 || N == 0) return FA_OK;
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ARG;
-  fa::FwdArgs a{q, k, v, o, lse, nullptr, B, H, Hkv, N, N, d, scale, causal != 0};
+  const fa::FwdArgs a = fwd_args(q, k, v, o, lse, nullptr, B, H, Hkv, N, N, N, d, scale, causal != 0, -1, -1);
   hipStream_t s = (hipStream_t)stream;
   return from_hip(dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(a, s) : fa::launch_fwd_f32(a, s));
 }
@@ -74,6 +109,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
                   int num_seqs, int total_tokens, int max_seqlen, int H, int Hkv, int d, float scale,
                   int causal, int dtype, void* stream) {
   if (num_seqs < 0 || total_tokens < 0 || max_seqlen < 0 || !heads_ok(H, Hkv)) return FA_ERR_SHAPE;
+  if (total_tokens > kMaxSeq) return FA_ERR_SHAPE;
   if (max_seqlen > total_tokens) return FA_ERR_SHAPE;
   if (total_tokens > 0 && (max_seqlen == 0 || num_seqs == 0)) return FA_ERR_SHAPE;
   if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
@@ -83,7 +119,27 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
   if (total_tokens == 0) return FA_OK;
   if (!q || !k || !v || !o || !lse || !cu_seqlens) return FA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ARG;
-  fa::FwdArgs a{q, k, v, o, lse, cu_seqlens, num_seqs, H, Hkv, max_seqlen, total_tokens, d, scale, causal != 0};
+  // queries and keys of a packed sequence coincide, so bottom-right and top-left agree
+  const fa::FwdArgs a = fwd_args(q, k, v, o, lse, cu_seqlens, num_seqs, H, Hkv, max_seqlen, total_tokens,
+                                 max_seqlen, d, scale, causal != 0, -1, -1);
+  hipStream_t s = (hipStream_t)stream;
+  return from_hip(dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(a, s) : fa::launch_fwd_f32(a, s));
+}
+
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
+                  int Nq, int Nk, int d, float scale, int causal, int window_left, int window_right,
+                  int dtype, void* stream) {
+  if (B < 0 || Nq < 0 || Nk < 0 || Nq > kMaxSeq || Nk > kMaxSeq || !heads_ok(H, Hkv)) return FA_ERR_SHAPE;
+  if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32) return FA_ERR_DTYPE;
+  if (!scale_ok(scale) || (causal != 0 && causal != 1)) return FA_ERR_ARG;
+  if (window_left < -1 || window_right < -1 || (causal && window_right > 0)) return FA_ERR_ARG;
+  if (!fits(B, Nq, H, d) || !fits(B, Nk, Hkv, d)) return FA_ERR_SHAPE;
+  if (B == 0 || Nq == 0) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ARG;
+  const fa::FwdArgs a =
+      fwd_args(q, k, v, o, lse, nullptr, B, H, Hkv, Nq, Nq, Nk, d, scale, causal != 0, window_left, window_right);
   hipStream_t s = (hipStream_t)stream;
   return from_hip(dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(a, s) : fa::launch_fwd_f32(a, s));
 }

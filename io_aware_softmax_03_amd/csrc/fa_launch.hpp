@@ -20,8 +20,15 @@ struct FwdArgs {
   int total_rows;         // dense: N; packed: total_tokens (LSE row stride)
   int head_dim;
   float scale;
-  bool causal;
+  // Masking, bottom-right aligned: query i sees key j when i + lo_off <= j and, if banded,
+  // j <= i + hi_off. Causal square attention: banded, hi_off = 0, lo_off = kNoLowerBound.
+  int seqlen_k;  // dense: Nk (keys per sequence); packed: unused
+  bool banded;
+  int lo_off, hi_off;
 };
+
+// no lower bound: below -(every key position) for any length the entry points accept
+constexpr int kNoLowerBound = -(1 << 30);
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);

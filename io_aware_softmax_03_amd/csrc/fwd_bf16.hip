@@ -46,7 +46,10 @@ struct FwdKernelArgs {
   int heads;
   int kv_heads;    // K and V heads; query head h reads kv head h / group
   int group;       // heads / kv_heads
-  int seqlen;      // dense sequence length (unused for packed)
+  int seqlen;      // dense query sequence length (unused for packed)
+  int seqlen_k;    // dense key sequence length (unused for packed: queries and keys coincide)
+  // visible keys of query i: i + lo_off <= j (and j <= i + hi_off with CAUSAL), j < Lk
+  int lo_off, hi_off;
   int total_rows;  // LSE row stride for packed, N for dense
   int nqb;         // workgroups per (sequence, head): query blocks, or pairs of them if causal
   int grid;        // workgroups launched
@@ -89,7 +92,7 @@ __device__ __forceinline__ bf16x8 scale_bf16x8(const bf16x8& x, float alpha) {
   return pack_bf16x8(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN, bool WINDOW>
 __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) {
   constexpr int KK = D / 16;                 // MFMA k-steps over the head dim
   constexpr int DB = D / 32;                 // 32-wide output blocks over the head dim
@@ -143,13 +146,17 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
     h = bh % p.heads;
     bs = bh / p.heads;
   }
-  int seq_start, L;
+  int seq_start, seq_start_k, L, Lk;  // L: query rows
   if constexpr (VARLEN) {
     seq_start = p.cu_seqlens[bs];
     L = p.cu_seqlens[bs + 1] - seq_start;
+    seq_start_k = seq_start;
+    Lk = L;
   } else {
     seq_start = bs * p.seqlen;
     L = p.seqlen;
+    seq_start_k = bs * p.seqlen_k;
+    Lk = p.seqlen_k;
   }
   const int nb = (L + kBR - 1) / kBR;
 
@@ -165,7 +172,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
     const int rs = p.heads * D;     // Q / O row stride in elements (< 2^31 by the host checks)
     const int rsk = p.kv_heads * D; // K / V row stride
     const size_t base = ((size_t)seq_start * p.heads + h) * D;
-    const size_t base_kv = ((size_t)seq_start * p.kv_heads + h / p.group) * D;
+    const size_t base_kv = ((size_t)seq_start_k * p.kv_heads + h / p.group) * D;
     const uint16_t* __restrict__ qg = p.q + base;
     const uint16_t* __restrict__ kg = p.k + base_kv;
     const uint16_t* __restrict__ vg = p.v + base_kv;
@@ -190,12 +197,25 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+a"(qf[g][kk]));
 
-    int ntiles = (L + kBC - 1) / kBC;
-    if constexpr (CAUSAL) ntiles = min(ntiles, (min(q0 + kBR, L) - 1) / kBC + 1);
-    // key blocks this wave computes (causal: those with a key its rows can see); every wave
-    // takes part in all of the block's loads and barriers
+    // key blocks t0 .. t0 + ntiles - 1 of this query block: from the block holding the first
+    // row's lowest visible key to the one holding the last row's highest (blocks outside
+    // hold no visible key and are skipped)
+    const int kfirst = WINDOW ? max(0, q0 + p.lo_off) : 0;
+    const int klast = CAUSAL ? min(Lk - 1, min(q0 + kBR, L) - 1 + p.hi_off) : Lk - 1;
+    const int t0 = kfirst / kBC;
+    const int ntiles = klast >= kfirst ? klast / kBC + 1 - t0 : 0;
+    const int kb0 = t0 * kBC;
+    // key blocks this wave computes (upper bound: the last one with a key its rows can see);
+    // every wave takes part in all of the block's loads and barriers
     int wtiles = 0;
-    if (wave_active) wtiles = CAUSAL ? min(ntiles, min(qw + kQW - 1, L - 1) / kBC + 1) : ntiles;
+    if (wave_active) {
+      const int wlast = CAUSAL ? min(Lk - 1, min(qw + kQW - 1, L - 1) + p.hi_off) : Lk - 1;
+      wtiles = wlast >= kb0 ? min(ntiles, wlast / kBC + 1 - t0) : 0;
+    }
+    // first key block this wave computes (window: the one holding its first row's lowest
+    // visible key); before it the wave only takes part in the loads and barriers
+    int ws = 0;
+    if constexpr (WINDOW) ws = min(wtiles, max(0, qw + p.lo_off) / kBC - t0);
 
     // ---- staging: wave-load `it` of this wave fills tile rows
     // lrow = (wid*LOADS + it) * ROWS_PER_KB + lane / CH at physical chunk lane % CH; the lane
@@ -210,11 +230,11 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
       k_src[it] = (unsigned)(lrow * rsk + (phys ^ swz_k<D>(lrow)) * 8) * 2u;
       v_src[it] = (unsigned)(lrow * rsk + (phys ^ swz_v<D>(lrow)) * 8) * 2u;
     }
-    // copy key block kt of K (IS_K) or V into buffer BUF
+    // copy key block t0 + kt of K (IS_K) or V into buffer BUF
     auto issue = [&](auto is_kc, auto bufc, int kt) {
       constexpr bool IS_K = decltype(is_kc)::value;
-      const int k0 = kt * kBC;
-      const unsigned bytes = (unsigned)(min(kBC - 1, L - 1 - k0) * rsk + D) * 2u;
+      const int k0 = kb0 + kt * kBC;
+      const unsigned bytes = (unsigned)(min(kBC - 1, Lk - 1 - k0) * rsk + D) * 2u;
       const __amdgpu_buffer_rsrc_t src = make_rsrc((IS_K ? kg : vg) + (size_t)k0 * rsk, bytes);
       char* dst = (IS_K ? kbuf(bufc) : vbuf(bufc)) + wid * LOADS * 1024;
 #pragma unroll
@@ -276,15 +296,20 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
     const float c2 = p.scale_log2;
 
     // score s[g][i] of a block is S^T[key k0 + 8(i/4) + 4hh + i%4][query qw + 32g + r]
-    auto edge = [&](int k0) { return (CAUSAL && k0 + kBC - 1 > qw) || (k0 + kBC > L); };
+    auto edge = [&](int k0) {
+      return (CAUSAL && k0 + kBC - 1 > qw + p.hi_off) || (k0 + kBC > Lk) ||
+             (WINDOW && k0 < qw + kQW - 1 + p.lo_off);
+    };
     auto mask = [&](f32x16 (&s)[2], int k0) {
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        const int lim = CAUSAL ? min(qw + 32 * g + r, L - 1) : L - 1;  // last visible key
+        const int row = qw + 32 * g + r;
+        const int lim = CAUSAL ? min(row + p.hi_off, Lk - 1) : Lk - 1;  // last visible key
+        const int low = row + p.lo_off;                                  // first visible key
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int kl = k0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          s[g][i] = kl > lim ? -INFINITY : s[g][i];
+          s[g][i] = (kl > lim || (WINDOW && kl < low)) ? -INFINITY : s[g][i];
         }
       }
     };
@@ -386,7 +411,9 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
     using VT = std::integral_constant<bool, false>;
 
     // ---- prologue: K(0) -> K buffer 0, K(1) -> K buffer 1; V buffer 1 is cleared so the
-    // first step's P V (a zero P block times that buffer) adds exact zeros
+    // first step's P V (a zero P block times that buffer) adds exact zeros. A block whose
+    // rows see no key at all skips to the epilogue (zeros, LSE -inf).
+    if (ntiles > 0) {
     issue(KT(), B0(), 0);
     issue(KT(), B1(), min(1, ntiles - 1));
     {
@@ -402,10 +429,10 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
       for (int ks = 0; ks < KS; ++ks) pB[g][ks] = bf16x8{};
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (wtiles > 0) {
+    if (ws == 0 && wtiles > 0) {
       qk(sA, B0());
       asm volatile("" : "+v"(sA[0]), "+v"(sA[1]));
-      if (edge(0)) mask(sA, 0);
+      if (edge(kb0)) mask(sA, kb0);
       const float mt[2] = {rowmax(sA[0]), rowmax(sA[1])};
       repivot(mt, pB);
     }
@@ -548,8 +575,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
       __builtin_amdgcn_sched_barrier(0);
       if (j + 1 < wtiles) {
         // a diagonal or ragged block is masked, and its maximum taken, only now
-        if (edge((j + 1) * kBC)) {
-          mask(n, (j + 1) * kBC);
+        if (edge(kb0 + (j + 1) * kBC)) {
+          mask(n, kb0 + (j + 1) * kBC);
           mt[0] = rowmax(n[0]);
           mt[1] = rowmax(n[1]);
         }
@@ -566,21 +593,64 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     };
+    // step j - 1 of a wave whose first block is j (window): that step's loads, then S(j)
+    // from K buffer j&1, formed as the prologue forms S(0); P(j-1) is zero
+    auto pre_step = [&](auto phase, int j) {
+      constexpr int PH = decltype(phase)::value;
+      constexpr bool ODD = PH & 1;
+      f32x16(&n)[2] = ODD ? sA : sB;       // S(j+1), where step j+1 reads it
+      bf16x8(&pz)[2][KS] = ODD ? pB : pA;  // P(j), step j+1's previous block
+      issue(KT(), std::integral_constant<int, PH>(), min(j + 2, ntiles - 1));
+      issue(VT(), std::integral_constant<int, PH>(), j);
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) pz[g][ks] = bf16x8{};
+      qk(n, std::integral_constant<int, PH + 1>());
+      asm volatile("" : "+v"(n[0]), "+v"(n[1]));
+      if (edge(kb0 + (j + 1) * kBC)) mask(n, kb0 + (j + 1) * kBC);
+      const float mt[2] = {rowmax(n[0]), rowmax(n[1])};
+      repivot(mt, pz);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    };
     using F0 = std::integral_constant<int, 0>;
     using F1 = std::integral_constant<int, 1>;
-    // Every wave runs ntiles steps (the same barriers); only the first wtiles compute, and
-    // the last P block of the wave is multiplied into O right after them.
+    // Every wave runs ntiles steps (the same barriers); it computes blocks ws .. wtiles-1,
+    // and the last P block of the wave is multiplied into O right after them.
     int j = 0;
-    for (; j + 1 < wtiles; j += 2) {
-      step(F0(), j);
-      step(F1(), j + 1);
+    const bool computes = wtiles > ws;
+    if constexpr (WINDOW) {
+      if (computes && ws > 0) {
+        for (; j + 1 < ws; ++j) {
+          if (j & 1)
+            idle_step(F1(), j);
+          else
+            idle_step(F0(), j);
+        }
+        if (j & 1)
+          pre_step(F1(), j);
+        else
+          pre_step(F0(), j);
+        ++j;
+        if (j & 1) {  // keep the pairs below starting on an even block
+          step(F1(), j);
+          ++j;
+        }
+      }
     }
-    if (j < wtiles) {
-      step(F0(), j);
-      ++j;
-      pv_tail(pA, B0());  // wtiles odd: P(wtiles-1) is in pA, V(wtiles-1) in buffer 0
-    } else if (wtiles > 0) {
-      pv_tail(pB, B1());  // wtiles even: P(wtiles-1) is in pB, V(wtiles-1) in buffer 1
+    if (computes) {
+      for (; j + 1 < wtiles; j += 2) {
+        step(F0(), j);
+        step(F1(), j + 1);
+      }
+      if (j < wtiles) {
+        step(F0(), j);
+        ++j;
+        pv_tail(pA, B0());  // last block even: its P is in pA, its V in buffer 0
+      } else {
+        pv_tail(pB, B1());  // last block odd: its P is in pB, its V in buffer 1
+      }
     }
     for (; j < ntiles; ++j) {
       if (j & 1)
@@ -588,6 +658,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
       else
         idle_step(F0(), j);
     }
+    }  // ntiles > 0
 
     __builtin_amdgcn_s_waitcnt(0);  // no copy into LDS outlives the block
 
@@ -634,7 +705,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
   }
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN, bool WINDOW>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   FwdKernelArgs p;
   p.q = (const uint16_t*)a.q;
@@ -647,6 +718,9 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.kv_heads = a.kv_heads;
   p.group = a.heads / a.kv_heads;
   p.seqlen = a.seqlen;
+  p.seqlen_k = a.seqlen_k;
+  p.lo_off = a.lo_off;
+  p.hi_off = a.hi_off;
   p.total_rows = a.total_rows;
   const int nqb = (a.seqlen + kBR - 1) / kBR;
   p.nqb = CAUSAL ? (nqb + 1) / 2 : nqb;  // causal workgroups take a pair of query blocks
@@ -655,15 +729,18 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   p.grid = (int)blocks;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)blocks), dim3(kNW * 64), 0, stream, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, VARLEN, WINDOW>), dim3((unsigned)blocks), dim3(kNW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
   const bool varlen = a.cu_seqlens != nullptr;
-  if (a.causal) return varlen ? launch_t<D, true, true>(a, stream) : launch_t<D, true, false>(a, stream);
-  return varlen ? launch_t<D, false, true>(a, stream) : launch_t<D, false, false>(a, stream);
+  // a lower bound (sliding window) only for the dense layout: packed calls have none
+  if (!varlen && a.lo_off != kNoLowerBound)
+    return a.banded ? launch_t<D, true, false, true>(a, stream) : launch_t<D, false, false, true>(a, stream);
+  if (a.banded) return varlen ? launch_t<D, true, true, false>(a, stream) : launch_t<D, true, false, false>(a, stream);
+  return varlen ? launch_t<D, false, true, false>(a, stream) : launch_t<D, false, false, false>(a, stream);
 }
 
 }  // namespace

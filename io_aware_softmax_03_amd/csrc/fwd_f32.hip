@@ -22,7 +22,8 @@ struct F32Args {
   float* o;
   float* lse;
   const int* cu_seqlens;
-  int heads, kv_heads, group, seqlen, total_rows, nqb;
+  int heads, kv_heads, group, seqlen, seqlen_k, total_rows, nqb;
+  int lo_off, hi_off;  // visible keys of query i: i + lo_off <= j (and j <= i + hi_off if CAUSAL)
   float scale_log2;
 };
 
@@ -37,20 +38,24 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args p) {
   const int qb = p.nqb - 1 - (int)(group_id_x() % p.nqb);
   const int bh = group_id_x() / p.nqb;
   const int h = bh % p.heads, bs = bh / p.heads;
-  int seq_start, L;
+  int seq_start, seq_start_k, L, Lk;  // L: query rows, Lk: keys
   if constexpr (VARLEN) {
     seq_start = p.cu_seqlens[bs];
     L = p.cu_seqlens[bs + 1] - seq_start;
+    seq_start_k = seq_start;
+    Lk = L;
   } else {
     seq_start = bs * p.seqlen;
     L = p.seqlen;
+    seq_start_k = bs * p.seqlen_k;
+    Lk = p.seqlen_k;
   }
   const int q0 = qb * RPB;
   if (q0 >= L) return;
   const size_t rs = (size_t)p.heads * D;      // Q / O row stride
   const size_t rsk = (size_t)p.kv_heads * D;  // K / V row stride
   const size_t base = ((size_t)seq_start * p.heads + h) * D;
-  const size_t base_kv = ((size_t)seq_start * p.kv_heads + h / p.group) * D;
+  const size_t base_kv = ((size_t)seq_start_k * p.kv_heads + h / p.group) * D;
   const int tid = thread_id_x();
   const int part = tid % TPR;
   const int myq = q0 + tid / TPR;
@@ -64,14 +69,16 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args p) {
   }
   float m = -1e30f, l = 0.f;
 
-  int kv_end = L;
-  if constexpr (CAUSAL) kv_end = min(L, q0 + RPB);
-  for (int k0 = 0; k0 < kv_end; k0 += kKT) {
+  // keys any row of the block can see: from the first row's lowest to the last row's highest
+  int kv_end = Lk;
+  if constexpr (CAUSAL) kv_end = min(Lk, min(q0 + RPB, L) + p.hi_off);
+  const int kv_begin = max(0, q0 + p.lo_off) / kKT * kKT;
+  for (int k0 = kv_begin; k0 < kv_end; k0 += kKT) {
     __syncthreads();
     for (int e = tid; e < kKT * D; e += kThreads) {
       const int row = e / D, col = e % D;
       const int key = k0 + row;
-      const bool in = key < L;
+      const bool in = key < Lk;
       ks[e] = in ? p.k[base_kv + (size_t)key * rsk + col] : 0.f;
       vs[e] = in ? p.v[base_kv + (size_t)key * rsk + col] : 0.f;
     }
@@ -86,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args p) {
 #pragma unroll
       for (int off = 1; off < TPR; off <<= 1) acc += __shfl_xor(acc, off);
       const int key = k0 + j;
-      const bool keep = key < L && (!CAUSAL || key <= myq);
+      const bool keep = key < Lk && (!CAUSAL || key <= myq + p.hi_off) && key >= myq + p.lo_off;
       s[j] = keep ? acc * p.scale_log2 : -INFINITY;
       mt = fmaxf(mt, s[j]);
     }
@@ -135,6 +142,9 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.kv_heads = a.kv_heads;
   p.group = a.heads / a.kv_heads;
   p.seqlen = a.seqlen;
+  p.seqlen_k = a.seqlen_k;
+  p.lo_off = a.lo_off;
+  p.hi_off = a.hi_off;
   p.total_rows = a.total_rows;
   p.nqb = (a.seqlen + RPB - 1) / RPB;
   p.scale_log2 = a.scale * kLog2e;
@@ -148,7 +158,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
 template <int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
   const bool varlen = a.cu_seqlens != nullptr;
-  if (a.causal) return varlen ? launch_t<D, true, true>(a, stream) : launch_t<D, true, false>(a, stream);
+  if (a.banded) return varlen ? launch_t<D, true, true>(a, stream) : launch_t<D, true, false>(a, stream);
   return varlen ? launch_t<D, false, true>(a, stream) : launch_t<D, false, false>(a, stream);
 }
 

@@ -83,6 +83,29 @@ def test_fwd_empty_is_noop():
     assert fwd(N=0, q=None, k=None, v=None, o=None, lse=None) == _clib.FA_OK
 
 
+def fwd_window(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=4, Hkv=2, Nq=16, Nk=64, d=128, scale=0.1,
+             causal=1, left=-1, right=-1, dtype=_clib.FA_DTYPE_BF16, stream=None)
+    a.update(kw)
+    return _clib.lib().fa_fwd_window(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Nq=-1), _clib.FA_ERR_SHAPE), (dict(Nk=-1), _clib.FA_ERR_SHAPE), (dict(Nq=(1 << 30) + 1), _clib.FA_ERR_SHAPE),
+    (dict(Nk=(1 << 30) + 1), _clib.FA_ERR_SHAPE), (dict(Hkv=3), _clib.FA_ERR_SHAPE), (dict(left=-2), _clib.FA_ERR_ARG),
+    (dict(right=-5), _clib.FA_ERR_ARG), (dict(right=3), _clib.FA_ERR_ARG), (dict(causal=2), _clib.FA_ERR_ARG),
+    (dict(d=80), _clib.FA_ERR_HEADDIM), (dict(dtype=9), _clib.FA_ERR_DTYPE), (dict(k=None), _clib.FA_ERR_NULL),
+    (dict(lse=FAKE + 4), _clib.FA_ERR_ARG), (dict(scale=float("inf")), _clib.FA_ERR_ARG),
+])
+def test_fwd_window_rejects(kw, code):
+    assert fwd_window(**kw) == code
+
+
+def test_fwd_window_accepts_upper_window_without_causal_and_empty_queries():
+    assert fwd_window(Nq=0, q=None, k=None, v=None, o=None, lse=None) == _clib.FA_OK
+    assert fwd_window(B=0, causal=0, right=3, q=None, k=None, v=None, o=None, lse=None) == _clib.FA_OK
+
+
 def varlen(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, cu=FAKE, num_seqs=2, total=10, max_seqlen=6, H=2,
              Hkv=2, d=128, scale=0.1, causal=1, dtype=_clib.FA_DTYPE_BF16, stream=None)
