@@ -265,6 +265,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1500)
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="skip reading the clock levels (rocm-smi); for runs under a profiler")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (untimed), so that a counter "
@@ -298,7 +300,7 @@ def main():
     step = lambda: fa.fwd(q, k, v, causal=True, out=(o, lse))  # noqa: E731
     wall_ms, kern_ms, kern_min = time_launches(step, args.steps, args.warmup)
     kern_median = time_launches.last_median
-    clocks = clocks_under_load(step)
+    clocks = None if args.no_clocks else clocks_under_load(step)
     flops = costs.fwd_flops(B, H, N, d, True)
     value = flops / (wall_ms * 1e-3) / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
