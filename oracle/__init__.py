@@ -12,6 +12,8 @@ the pages by eye:
 * ``attention``  — the definitions the GPU results are compared with:
   forward, packed variable-length forward, backward (exact gradient of the
   forward), single-token decode, decode against a paged cache.
+* ``fp8``        — the FP8 forward emulated step by step (rotation, block
+  quantization to e4m3, tiled online softmax with P quantized per block).
 * ``algorithms`` — the pages' algorithms written out step by step in float64
   (tiled online softmax, two-pass softmax, split-and-merge decoding, a scalar
   brute force). They exist to pin the definitions above and the pages' claims
@@ -27,6 +29,9 @@ backward, and the figures the pages print (``tests/golden``). No function is
 from .attention import (  # noqa: F401
     kv_head, band_keep, attention_head, attn_fwd, attn_fwd_window, attn_fwd_varlen, attn_bwd_head, attn_bwd,
     attn_decode, attn_decode_slice, attn_decode_paged,
+)
+from .fp8 import (  # noqa: F401
+    round_e4m3, hadamard, rotation, block_exponents, quantize_rows, fp8_attention_head, attn_fwd_fp8,
 )
 from .algorithms import (  # noqa: F401
     tiled_online_attention_head, softmax_two_pass, softmax_online,

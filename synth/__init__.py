@@ -8,5 +8,5 @@ from .inputs import (  # noqa: F401
     TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_DO,
     bf16_bits_from_f32, f32_from_bf16_bits, normal_slice, bnhd_tensor,
     varlen_lengths, cu_seqlens_from_lengths, varlen_tensor, decode_query,
-    paged_layout, paged_tensor,
+    paged_layout, paged_tensor, rademacher_signs, outlier_tensor,
 )

@@ -135,3 +135,24 @@ def paged_tensor(seed, tensor_id, seqlens, block_table, num_pages, page_size, H,
             t = np.arange(L)
             pool[block_table[b, t // page_size], t % page_size, h, :] = x
     return _finish(pool, dtype)
+
+
+def rademacher_signs(seed: int, d: int) -> np.ndarray:
+    """d independent +-1 values (float32), the random diagonal of an incoherence rotation."""
+    rng = np.random.default_rng([seed, 4711])
+    return np.where(rng.integers(0, 2, d) == 1, 1.0, -1.0).astype(np.float32)
+
+
+def outlier_tensor(seed, tensor_id, B, N, H, d, dtype="bf16", rate=1e-3, outlier_std=10.0):
+    """A [B, N, H, d] tensor whose entries are N(0, 1) plus, on a `rate` fraction of entries
+    chosen independently, an extra N(0, outlier_std^2) term (the FP8 outlier test:
+    N(0, 100) on 0.1% of entries)."""
+    out = np.empty((B, N, H, d), dtype=np.float32)
+    for b in range(B):
+        for h in range(H):
+            x = normal_slice(seed, tensor_id, b, h, (N, d))
+            rng = np.random.default_rng([seed, tensor_id, b, h, 313])
+            hit = rng.random((N, d)) < rate
+            x = x + np.where(hit, rng.standard_normal((N, d)).astype(np.float32) * np.float32(outlier_std), 0)
+            out[b, :, h, :] = x
+    return _finish(out, dtype)
