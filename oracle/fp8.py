@@ -16,10 +16,17 @@ the second FP8 product).
 Readings where the page is silent (each listed in the design notes):
 * e4m3 is the OCP "fn" format: no infinities, subnormals down to 2^-9, largest 448;
   conversion rounds to nearest, ties to even, and saturates at +-448.
-* R = H_d D / sqrt(d) (Sylvester Hadamard H_d, D = diag(signs)); a row x becomes x R.
-* A block's scale is the power of two 2^e with e = ceil(log2(amax / 448)) (amax = 0: e = 0),
-  so dividing by it is exact and the block's largest magnitude lands in [224, 448].
-  Blocks are 64 consecutive rows (tokens) of one head, for Q, K and V alike.
+* R = H_d D / sqrt(d) (Sylvester Hadamard H_d, D = diag(signs)); a row x becomes x R. The
+  rotated row that gets quantized is y = (x H_d) D, without the 1/sqrt(d): (qR)(kR)^T =
+  y_q y_k^T / d, so 1/d joins the score scale (a power of two for d = 64, 128). x H_d is
+  formed by the fast Walsh-Hadamard transform in float32, butterflies (a, b) -> (a + b,
+  a - b) at strides 1, 2, 4, ..., d/2 in that order: a quantized code is an integer the
+  float arithmetic decides, so the emulation takes that decision in the kernel's precision
+  and order (IEEE float32 additions give the same result on both sides).
+* A block's scale is the power of two 2^e with e the smallest integer such that
+  amax <= 448 * 2^e (amax = 0: e = 0), so dividing by it is exact and the block's largest
+  magnitude lands in (224, 448]. Blocks are 64 consecutive rows (tokens) of one head, for
+  Q, K and V alike.
 * P is quantized per key block as the online algorithm forms it: P~ = exp(S - m_new) in
   (0, 1] against the running maximum, times 2^8, rounded to e4m3, divided by 2^8. The row
   sum l and the LSE use the unquantized P~; O~ accumulates the quantized P times V.
@@ -63,11 +70,43 @@ def hadamard(d: int) -> np.ndarray:
     return h
 
 
+def fwht_f32(x) -> np.ndarray:
+    """x H_d for the rows of x (last axis, a power of two), in float32 butterflies at
+    strides 1, 2, ..., d/2 (the fast Walsh-Hadamard transform)."""
+    y = np.array(x, dtype=np.float32, copy=True)
+    d = y.shape[-1]
+    if d < 1 or d & (d - 1):
+        raise ValueError("d must be a power of two")
+    h = 1
+    while h < d:
+        z = y.reshape(y.shape[:-1] + (d // (2 * h), 2, h))
+        a, b = z[..., 0, :].copy(), z[..., 1, :].copy()
+        z[..., 0, :] = a + b
+        z[..., 1, :] = a - b
+        y = z.reshape(y.shape)
+        h *= 2
+    return y
+
+
+def rotate_unnormalised(x, signs) -> np.ndarray:
+    """(x H_d) D in float32: the rotated rows before quantization (x R times sqrt(d))."""
+    return fwht_f32(x) * np.asarray(signs, dtype=np.float32)
+
+
 def rotation(signs) -> np.ndarray:
     """R = H_d diag(signs) / sqrt(d), orthogonal for any +-1 signs."""
     s = np.asarray(signs, dtype=np.float64)
     d = s.shape[0]
     return hadamard(d) * s[None, :] / math.sqrt(d)
+
+
+def scale_exponent(amax: float) -> int:
+    """Smallest e with amax <= 448 * 2^e (0 for amax = 0). With amax = f 2^E, f in [0.5, 1)
+    and 448 = 0.875 * 2^9: e = E - 9 when f <= 0.875, else E - 8."""
+    if amax <= 0:
+        return 0
+    f, E = math.frexp(float(amax))
+    return E - 9 if f <= 0.875 else E - 8
 
 
 def block_exponents(x, block_rows: int) -> np.ndarray:
@@ -76,8 +115,7 @@ def block_exponents(x, block_rows: int) -> np.ndarray:
     nb = -(-x.shape[0] // block_rows)
     e = np.zeros(nb, dtype=np.int64)
     for b in range(nb):
-        amax = np.abs(x[b * block_rows:(b + 1) * block_rows]).max(initial=0.0)
-        e[b] = math.ceil(math.log2(amax / E4M3_MAX)) if amax > 0 else 0
+        e[b] = scale_exponent(np.abs(x[b * block_rows:(b + 1) * block_rows]).max(initial=0.0))
     return e
 
 
@@ -100,8 +138,11 @@ def fp8_attention_head(q, k, v, scale, causal=False, signs=None, block_rows=64, 
     block_rows >= the length gives one scale per tensor slice."""
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     if signs is not None:
-        R = rotation(signs)
-        q, k = q @ R, k @ R
+        # x R = (x H D) / sqrt(d): rotate without the normalisation, put 1/d on the scores
+        d = q.shape[1]
+        q = rotate_unnormalised(q, signs).astype(np.float64)
+        k = rotate_unnormalised(k, signs).astype(np.float64)
+        scale = float(scale) / d
     if quantize:
         q, _ = quantize_rows(q, block_rows)
         k, _ = quantize_rows(k, block_rows)

@@ -71,6 +71,27 @@ def test_hadamard_and_rotation():
     np.testing.assert_allclose((q @ R) @ (k @ R).T, q @ k.T, atol=1e-12)
 
 
+def test_fwht_is_the_hadamard_product():
+    """The float32 butterflies give x H_d to float32 rounding (exactly, for small integers)."""
+    rng = np.random.default_rng(7)
+    for d in (4, 64, 128):
+        xi = rng.integers(-20, 21, (9, d)).astype(np.float32)
+        np.testing.assert_array_equal(oracle.fwht_f32(xi), (xi.astype(np.float64) @ scipy.linalg.hadamard(d)))
+        x = rng.standard_normal((9, d)).astype(np.float32)
+        np.testing.assert_allclose(oracle.fwht_f32(x), x.astype(np.float64) @ scipy.linalg.hadamard(d),
+                                   rtol=0, atol=1e-4)
+        s = synth.rademacher_signs(1, d)
+        np.testing.assert_allclose(oracle.rotate_unnormalised(x, s) / math.sqrt(d), x @ oracle.rotation(s),
+                                   rtol=0, atol=1e-5)
+
+
+def test_scale_exponent_is_the_smallest_sufficient_power():
+    for amax in [448.0, 448.0001, 224.0, 224.0001, 1.0, 0.875 * 2 ** -3, 3.5, 1e-30, 7e5]:
+        e = oracle.scale_exponent(amax)
+        assert amax <= 448 * 2.0 ** e and amax > 448 * 2.0 ** (e - 1)
+    assert oracle.scale_exponent(0.0) == 0
+
+
 def test_block_quantization_scales():
     x = synth.f32_from_bf16_bits(synth.outlier_tensor(2, 0, 1, 300, 1, 128))[0, :, 0].astype(np.float64)
     xq, e = oracle.quantize_rows(x, 64)
@@ -78,7 +99,7 @@ def test_block_quantization_scales():
     for b in range(5):
         blk = x[64 * b:64 * (b + 1)]
         top = np.abs(blk).max() / 2.0 ** e[b]
-        assert 224 <= top <= 448
+        assert 224 < top <= 448
     # every value is an e4m3 value times its block's power of two
     t = e4m3_table()
     scaled = np.abs(xq) / np.repeat(np.exp2(e.astype(float)), 64)[:300, None]
@@ -94,10 +115,12 @@ def test_block_quantization_scales():
 def test_unquantized_emulation_is_exact_attention(causal):
     q, k, v = np.random.default_rng(2).standard_normal((3, 150, 32))
     ref = oracle.attention_head(q, k, v, 0.2, causal)
-    for signs in (None, synth.rademacher_signs(5, 32)):
+    # without the rotation: float64 throughout, exact; with it: the rotation is formed in
+    # float32 (the kernel's precision), so the scores move by float32 rounding only
+    for signs, tol in ((None, 1e-12), (synth.rademacher_signs(5, 32), 1e-5)):
         got = oracle.fp8_attention_head(q, k, v, 0.2, causal, signs, quantize=False)
-        np.testing.assert_allclose(got[0], ref[0], atol=1e-12)
-        np.testing.assert_allclose(got[1], ref[1], atol=1e-12)
+        np.testing.assert_allclose(got[0], ref[0], atol=tol)
+        np.testing.assert_allclose(got[1], ref[1], atol=tol)
 
 
 def outlier_rmse(**kw):
@@ -109,7 +132,7 @@ def outlier_rmse(**kw):
 
 
 def test_page_outlier_experiment():
-    """Rotation + block scales: 7.3e-3 here (the page: 9.1e-3); without rotation 1.3e-2
+    """Rotation + block scales: 7.4e-3 here (the page: 9.1e-3); without rotation 1.3e-2
     (the page: 2.4e-2); block against per-tensor scales: no visible change (the page: 9.1e-3
     against 9.3e-3; power-of-two scales move whole binades, so only underflow differs)."""
     s = synth.rademacher_signs(5, 128)
@@ -126,7 +149,7 @@ def test_planted_mistakes_are_caught(monkeypatch):
     q, k, v = np.random.default_rng(3).standard_normal((3, 100, 32))
     ref = oracle.attention_head(q, k, v, 0.2, True)
     s = synth.rademacher_signs(6, 32)
-    # rotating Q but not K changes the scores: the exactness pin fails
+    # rotating Q but not K changes the scores
     R = fp8.rotation(s)
     got = oracle.attention_head(q @ R, k, v, 0.2, True)
     assert np.max(np.abs(got[0] - ref[0])) > 1e-3
