@@ -156,6 +156,39 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            int B, int H, int N, int d, float scale, int causal, int dtype,
            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of workspace fa_fwd_fp8 needs: the e4m3 codes of Q, K and V (one byte per
+ * element, rows padded to a multiple of 64) and one int32 exponent per 64-row block of
+ * each. 0 for invalid sizes. */
+size_t fa_fwd_fp8_workspace_bytes(int B, int H, int Hkv, int N, int d);
+
+/*
+ * fa_fwd_fp8 — forward attention computed in FP8 e4m3 ("FlashAttention-2 and -3",
+ * section "FP8, and the outlier problem"), same inputs and outputs as fa_fwd with
+ * dtype FA_DTYPE_BF16:
+ *   q [B, N, H, d], k, v [B, N, Hkv, d] bf16; o [B, N, H, d] bf16; lse fp32 [B, H, N]
+ *   signs     device fp32 [d] of +1/-1, or NULL. Given, Q and K are first rotated by
+ *             R = H_d diag(signs) / sqrt(d) (incoherent processing: the scores are
+ *             unchanged in exact arithmetic, outliers are spread over all coordinates).
+ *   Each block of 64 rows of one head of Q, K and V gets its own power-of-two scale
+ *   (block quantization); P is quantized to e4m3 before the second product; both
+ *   products run on the FP8 matrix cores with fp32 accumulation; the softmax runs in
+ *   fp32. O approximates exact attention to FP8 accuracy, not to bf16 accuracy.
+ *   workspace  at least fa_fwd_fp8_workspace_bytes(B, H, Hkv, N, d) bytes, 256-byte
+ *              aligned; overwritten. After the call it holds the quantized operands,
+ *              with Np = N rounded up to a multiple of 64, nb = Np / 64 and each part
+ *              starting at the next multiple of 256 bytes: Q codes [B, H, Np, d],
+ *              K codes [B, Hkv, Np, d] (rotated when signs are given), V codes per
+ *              64-key block transposed [B, Hkv, nb, d, 64] with slot s holding key
+ *              32*((s>>4)&1) + 8*((s>>2)&3) + 4*(s>>5) + (s&3) of the block, then int32
+ *              exponents [B, H, nb], [B, Hkv, nb], [B, Hkv, nb]: a block's values are
+ *              its e4m3 codes (OCP, bias 7) times 2^exponent.
+ * Causal is top-left (square). The call enqueues three quantization launches and the
+ * attention launch.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, const float* signs, void* o, float* lse,
+               int B, int H, int Hkv, int N, int d, float scale, int causal,
+               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace fa_decode needs for `num_splits` partials per (batch, head):
  * fp32 running max, running sum and a d-wide partial output for each. */
 size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits);

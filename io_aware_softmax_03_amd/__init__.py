@@ -8,6 +8,7 @@ memory and streams. Tensors must be contiguous device tensors:
     fwd(q, k, v, scale=None, causal=False) -> (o, lse)          q [B, N, H, d], k,v [B, N, Hkv, d]
     fwd_window(q, k, v, scale=None, causal=False, window=(-1, -1)) -> (o, lse)
                                                  q [B, Nq, H, d], k,v [B, Nk, Hkv, d]
+    fwd_fp8(q, k, v, signs=None, scale=None, causal=False) -> (o, lse)   FP8 e4m3 compute
     fwd_varlen(q, k, v, cu_seqlens, max_seqlen, ...) -> (o, lse) q [T, H, d], k,v [T, Hkv, d]
     bwd(q, k, v, o, lse, do, scale=None, causal=False) -> (dq, dk, dv)   fp32 grads
     decode(q, k_cache, v_cache, scale=None, num_splits=64) -> (o, lse)   q [B, H, d]
@@ -25,7 +26,7 @@ from ._clib import (  # noqa: F401
     FAError, FA_DTYPE_BF16, FA_DTYPE_F32, check, lib, strerror,
 )
 
-__all__ = ["fwd", "fwd_window", "fwd_varlen", "bwd", "decode", "decode_paged", "FAError", "lib"]
+__all__ = ["fwd", "fwd_window", "fwd_fp8", "fwd_varlen", "bwd", "decode", "decode_paged", "FAError", "lib"]
 
 
 def _torch():
@@ -110,6 +111,40 @@ def fwd_window(q, k, v, scale=None, causal=False, window=(-1, -1), out=None):
                              B, H, Hkv, Nq, Nk, d, _scale(scale, d), int(bool(causal)), left, right,
                              _dtype_code(q), _stream(q.device))
     check(st, "fa_fwd_window")
+    return o, lse
+
+
+def fwd_fp8(q, k, v, signs=None, scale=None, causal=False, out=None, workspace=None):
+    """Forward computed in FP8 e4m3 with block quantization, and incoherent processing when
+    ``signs`` (a device fp32 [d] tensor of +-1) is given. q [B, N, H, d], k, v [B, N, Hkv, d],
+    all bf16. Returns O [B, N, H, d] bf16 and fp32 LSE [B, H, N]."""
+    torch = _torch()
+    _require((q, k, v), ("q", "k", "v"))
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
+        raise ValueError("q must be [B, N, H, d] and k, v [B, N, Hkv, d]")
+    if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("fwd_fp8 takes bfloat16 q, k, v")
+    B, N, H, d = q.shape
+    Hkv = k.shape[2]
+    if signs is not None:
+        _require((signs,), ("signs",))
+        if signs.dtype != torch.float32 or signs.shape != (d,):
+            raise ValueError("signs must be a float32 [d] tensor")
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        _require((o, lse), ("o", "lse"))
+        if o.shape != q.shape or o.dtype != q.dtype or lse.shape != (B, H, N) or lse.dtype != torch.float32:
+            raise ValueError("out must be (o [B, N, H, d] like q, lse fp32 [B, H, N])")
+    nbytes = lib().fa_fwd_fp8_workspace_bytes(B, H, Hkv, N, d)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    st = lib().fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), None if signs is None else signs.data_ptr(),
+                          o.data_ptr(), lse.data_ptr(), B, H, Hkv, N, d, _scale(scale, d), int(bool(causal)),
+                          workspace.data_ptr(), workspace.numel(), _stream(q.device))
+    check(st, "fa_fwd_fp8")
     return o, lse
 
 

@@ -144,6 +144,28 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* l
   return from_hip(dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(a, s) : fa::launch_fwd_f32(a, s));
 }
 
+size_t fa_fwd_fp8_workspace_bytes(int B, int H, int Hkv, int N, int d) {
+  if (B < 0 || N < 0 || !heads_ok(H, Hkv) || !head_dim_ok(d) || N > kMaxSeq) return 0;
+  return fa::fp8_layout(B, H, Hkv, N, d).total;
+}
+
+int fa_fwd_fp8(const void* q, const void* k, const void* v, const float* signs, void* o, float* lse, int B,
+               int H, int Hkv, int N, int d, float scale, int causal, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  if (B < 0 || N < 0 || N > kMaxSeq || !heads_ok(H, Hkv)) return FA_ERR_SHAPE;
+  if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
+  if (!scale_ok(scale) || (causal != 0 && causal != 1)) return FA_ERR_ARG;
+  if (!fits(B, N, H, d)) return FA_ERR_SHAPE;
+  if (B == 0 || N == 0) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (!workspace || workspace_bytes < fa_fwd_fp8_workspace_bytes(B, H, Hkv, N, d)) return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      ((uintptr_t)workspace & 255u) != 0 || ((uintptr_t)signs & 3u) != 0)
+    return FA_ERR_ARG;
+  fa::Fp8Args a{q, k, v, signs, o, lse, workspace, B, H, Hkv, N, d, scale, causal != 0};
+  return from_hip(fa::launch_fwd_fp8(a, (hipStream_t)stream));
+}
+
 size_t fa_bwd_workspace_bytes(int B, int H, int N) {
   if (B < 0 || H < 0 || N < 0) return 0;
   return 2 * (size_t)B * H * N * sizeof(float);

@@ -69,4 +69,27 @@ struct DecodeArgs {
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 
+// FP8 forward: bf16 Q, K, V are quantized into the workspace, then attended in e4m3.
+struct Fp8Args {
+  const void* q;       // bf16 [B, N, H, d]
+  const void* k;       // bf16 [B, N, Hkv, d]
+  const void* v;
+  const float* signs;  // [d] of +-1: rotate Q and K; NULL: no rotation
+  void* o;             // bf16 [B, N, H, d]
+  float* lse;          // [B, H, N]
+  void* workspace;     // fp8_layout(...).total bytes, 256-byte aligned
+  int batch, heads, kv_heads, seqlen, head_dim;
+  float scale;
+  bool causal;
+};
+
+// byte offsets inside the FP8 workspace: codes of Q [B, H, Np, d], K [B, Hkv, Np, d],
+// transposed V blocks [B, Hkv, Np / 64, d, 64], then int32 exponents per 64-row block
+struct Fp8Layout {
+  size_t q8, k8, v8t, eq, ek, ev, total;
+};
+Fp8Layout fp8_layout(int B, int H, int Hkv, int N, int d);
+
+hipError_t launch_fwd_fp8(const Fp8Args& a, hipStream_t stream);
+
 }  // namespace fa

@@ -1,0 +1,416 @@
+// FP8 forward attention ("FlashAttention-2 and -3", section "FP8, and the outlier problem").
+//
+// Two kernels after one another on the caller's stream:
+//
+// 1. fp8_quant_kernel, once each for Q, K and V: one workgroup per block of 64 rows of one
+//    head. Q and K rows are optionally rotated by R = H_d D / sqrt(d) (incoherent
+//    processing: Hadamard matrix times a random +-1 diagonal). The kernel forms x H_d D with
+//    the fast Walsh-Hadamard transform in fp32 (butterflies at strides 1, 2, ..., d/2) and
+//    leaves the 1/sqrt(d) to the score scale (1/d there). Each block gets one power-of-two
+//    scale 2^e, the smallest with amax <= 448 * 2^e (block quantization), and every value
+//    becomes the e4m3 code of x * 2^-e (exact scaling, round to nearest even). Q and K
+//    codes are stored head-major, [B, H, rows, d]; V codes are stored per 64-key block
+//    transposed, [B, H, block, d, 64], with the keys of a block in the order the attention
+//    kernel's P registers hold them, so each lane's V^T operand is 32 contiguous bytes.
+// 2. fwd_fp8_kernel: 4 independent waves of 64 query rows (two groups of 32) per workgroup;
+//    per 64-key block, S^T = K Q^T and O^T += V^T P^T on v_mfma_scale_f32_32x32x64_f8f6f4,
+//    the online softmax in fp32 (base 2), and P quantized to e4m3 as P * 2^8. The block
+//    scales enter exactly: 2^(eq + ek) on the score scale, 2^ev and 2^-8 through the
+//    MFMA's E8M0 operand scales. The row sum and the LSE use the unquantized P.
+//
+// Operand layouts of v_mfma_scale_f32_32x32x64_f8f6f4 with e4m3 operands (lane l, r = l%32,
+// hh = l/32): A row r, B column r; the 32 bytes of a lane are 32 of the 64 k indices, and A
+// and B are paired by (hh, byte), so any k order used for both operands is the same product.
+// C: lane holds C[8i + 4hh + j][r] at acc[4i + j] (as for the bf16 32x32 products).
+#include "fa_device.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kRows = 64;  // quantization block and key block
+constexpr int kPScaleLog2 = 8;
+
+// x * 2^-e rounded to e4m3 (pairs; lo byte first)
+__device__ __forceinline__ uint32_t cvt4_fp8(float a, float b, float c, float d, int e) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(a, -e), __builtin_amdgcn_ldexpf(b, -e), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(c, -e), __builtin_amdgcn_ldexpf(d, -e), w, true);
+  return (uint32_t)w;
+}
+
+struct QuantArgs {
+  const uint16_t* x;   // bf16 [B, N, Hx, d]
+  const float* signs;  // [d] of +-1 (rotation) or unused
+  uint8_t* out;        // rows: [B, Hx, nblk * 64, d]; transposed V: [B, Hx, nblk, d, 64]
+  int* exps;           // [B, Hx, nblk]
+  int heads, seqlen, nblk;
+};
+
+// key slot (0..63) of the transposed V block -> key within the block. The attention kernel
+// packs the 32 probabilities a lane holds for keys 32t + 8i + 4hh + j as bytes 16t + 4i + j
+// of its B operand in lane half hh; V^T must hold the same key at slot 32hh + 16t + 4i + j.
+__device__ __forceinline__ int slot_key(int s) {
+  const int hh = s >> 5, t = (s >> 4) & 1, i = (s >> 2) & 3, j = s & 3;
+  return 32 * t + 8 * i + 4 * hh + j;
+}
+
+template <int D, bool ROTATE, bool VT>
+__global__ __launch_bounds__(256) void fp8_quant_kernel(QuantArgs p) {
+  constexpr int EPT = D / 4;  // elements per thread: each row is spread over 4 threads
+  __shared__ float red[4];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[VT ? kRows * D : 16];
+  const int w = group_id_x();
+  const int blk = w % p.nblk;
+  const int bh = w / p.nblk;
+  const int h = bh % p.heads, b = bh / p.heads;
+  const int t = thread_id_x();
+  const int r = t >> 2, part = t & 3;
+  const int row = blk * kRows + r;
+
+  float y[EPT];
+  if (row < p.seqlen) {
+    const uint16_t* src = p.x + (((size_t)b * p.seqlen + row) * p.heads + h) * D + part * EPT;
+#pragma unroll
+    for (int c = 0; c < EPT / 8; ++c) {
+      const u32x4 v = *(const u32x4*)(src + 8 * c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y[8 * c + 2 * e] = bf16_lo(v[e]);
+        y[8 * c + 2 * e + 1] = bf16_hi(v[e]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) y[i] = 0.f;
+  }
+
+  if constexpr (ROTATE) {
+    // x H_d: butterflies (a, b) -> (a + b, a - b), strides 1 .. EPT/2 inside the thread,
+    // then EPT and 2 EPT between the row's four threads (adjacent lanes)
+#pragma unroll
+    for (int hs = 1; hs < EPT; hs <<= 1)
+#pragma unroll
+      for (int i = 0; i < EPT; ++i)
+        if ((i & hs) == 0) {
+          const float a = y[i], c = y[i + hs];
+          y[i] = a + c;
+          y[i + hs] = a - c;
+        }
+#pragma unroll
+    for (int m = 1; m < 4; m <<= 1) {
+      const bool upper = (part & m) != 0;
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        const float o = __shfl_xor(y[i], m);
+        y[i] = upper ? o - y[i] : y[i] + o;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) y[i] *= p.signs[part * EPT + i];
+  }
+
+  // block maximum magnitude -> exponent: smallest e with amax <= 448 * 2^e
+  float am = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) am = fmaxf(am, fabsf(y[i]));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+  if ((t & 63) == 0) red[t >> 6] = am;
+  __syncthreads();
+  am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  int e = 0;
+  if (am > 0.f) {
+    const int E = __builtin_amdgcn_frexp_expf(am);    // am = f * 2^E, f in [0.5, 1)
+    const float f = __builtin_amdgcn_frexp_mantf(am);
+    e = f <= 0.875f ? E - 9 : E - 8;                 // 448 = 0.875 * 2^9
+  }
+  if (t == 0) p.exps[bh * p.nblk + blk] = e;
+
+  uint32_t code[EPT / 4];
+#pragma unroll
+  for (int i = 0; i < EPT / 4; ++i) code[i] = cvt4_fp8(y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3], e);
+
+  if constexpr (!VT) {
+    uint8_t* dst = p.out + ((size_t)bh * p.nblk * kRows + row) * D + part * EPT;
+#pragma unroll
+    for (int c = 0; c < EPT / 16; ++c) {
+      u32x4 v = {code[4 * c], code[4 * c + 1], code[4 * c + 2], code[4 * c + 3]};
+      *(u32x4*)(dst + 16 * c) = v;
+    }
+  } else {
+    // stage the block's codes [key][dim] in LDS, then write it transposed: thread t covers
+    // 16 * (D / 64) consecutive bytes of the [d][64] block
+#pragma unroll
+    for (int c = 0; c < EPT / 16; ++c) {
+      u32x4 v = {code[4 * c], code[4 * c + 1], code[4 * c + 2], code[4 * c + 3]};
+      *(u32x4*)(tile + r * D + part * EPT + 16 * c) = v;
+    }
+    __syncthreads();
+    constexpr int BPT = D * kRows / 256;  // bytes per thread: 32 (D = 128) or 16 (D = 64)
+    const int o0 = t * BPT;
+    const int dim = o0 / kRows, s0 = o0 % kRows;
+    uint32_t wv[BPT / 4];
+#pragma unroll
+    for (int i = 0; i < BPT / 4; ++i) {
+      uint32_t x = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x |= (uint32_t)tile[slot_key(s0 + 4 * i + j) * D + dim] << (8 * j);
+      wv[i] = x;
+    }
+    uint8_t* dst = p.out + ((size_t)bh * p.nblk + blk) * D * kRows + o0;
+#pragma unroll
+    for (int c = 0; c < BPT / 16; ++c) {
+      u32x4 v = {wv[4 * c], wv[4 * c + 1], wv[4 * c + 2], wv[4 * c + 3]};
+      *(u32x4*)(dst + 16 * c) = v;
+    }
+  }
+}
+
+struct AttnArgs {
+  const uint8_t* q8;   // [B, H, Np, d]
+  const uint8_t* k8;   // [B, Hkv, Np, d]
+  const uint8_t* v8t;  // [B, Hkv, nblk, d, 64]
+  const int* eq;       // [B, H, nblk]
+  const int* ek;       // [B, Hkv, nblk]
+  const int* ev;       // [B, Hkv, nblk]
+  uint16_t* o;         // bf16 [B, N, H, d]
+  float* lse;          // [B, H, N]
+  int heads, kv_heads, group, seqlen, nblk, nqb;
+  float c2;            // scale * log2(e), divided by d when Q and K were rotated
+};
+
+__device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, const f32x16& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void fwd_fp8_kernel(AttnArgs p) {
+  constexpr int KS = D / 64;  // k-steps of S^T over the head dim
+  constexpr int DB = D / 32;  // 32-dim blocks of O^T
+  constexpr int QB = 256;     // query rows per workgroup
+  const int w = group_id_x();
+  const int pi = w % p.nqb;
+  const int bh = w / p.nqb;
+  const int h = bh % p.heads, bs = bh / p.heads;
+  const int hk = h / p.group;
+  const int N = p.seqlen;
+  const int nb = (N + QB - 1) / QB;
+  const size_t Np = (size_t)p.nblk * kRows;
+  const size_t qbase = ((size_t)bs * p.heads + h) * Np;   // row index of the head's first row
+  const size_t kbase = ((size_t)bs * p.kv_heads + hk) * Np;
+  const size_t vblk0 = ((size_t)bs * p.kv_heads + hk) * p.nblk;
+  const int* __restrict__ ekp = p.ek + ((size_t)bs * p.kv_heads + hk) * p.nblk;
+  const int* __restrict__ evp = p.ev + ((size_t)bs * p.kv_heads + hk) * p.nblk;
+
+  const int tid = thread_id_x();
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, r = lane & 31, hh = lane >> 5;
+
+  auto run_block = [&](int qb) {
+    const int qw = qb * QB + 64 * wid;  // this wave's first row
+    if (qw >= N) return;
+    const int eq = p.eq[((size_t)bs * p.heads + h) * p.nblk + qw / kRows];
+    // Q^T operands: query qw + 32g + r, dims 64ks + 32hh .. +31
+    i32x8 qf[2][KS];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qf[g][ks] = *(const i32x8*)(p.q8 + (qbase + qw + 32 * g + r) * D + 64 * ks + 32 * hh);
+
+    const int nkb = CAUSAL ? qw / kRows + 1 : p.nblk;
+    auto load = [&](int kb, i32x8 (&kd)[2][KS], i32x8 (&vd)[DB]) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          kd[t][ks] = *(const i32x8*)(p.k8 + (kbase + (size_t)kb * kRows + 32 * t + r) * D + 64 * ks + 32 * hh);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        vd[db] = *(const i32x8*)(p.v8t + ((vblk0 + kb) * D + 32 * db + r) * kRows + 32 * hh);
+    };
+
+    float m[2] = {-1e30f, -1e30f}, l[2] = {0.f, 0.f};
+    f32x16 oacc[2][DB];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[g][db][i] = 0.f;
+
+    // one 64-key block from operands kc, vc, with the next block's loads into kn, vn first
+    auto step = [&](int kb, const i32x8 (&kc)[2][KS], const i32x8 (&vc)[DB], i32x8 (&kn)[2][KS],
+                    i32x8 (&vn)[DB]) {
+      if (kb + 1 < nkb) load(kb + 1, kn, vn);
+      const float cs = __builtin_amdgcn_ldexpf(p.c2, eq + ekp[kb]);
+      const int sv = evp[kb] + 127;
+      // edge block: the causal diagonal or the ragged end
+      const bool edge = (CAUSAL && kb * kRows + kRows - 1 > qw) || (kb * kRows + kRows > N);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        // value 16t + 4i + j: score of key kb*64 + 32t + 8i + 4hh + j, query qw + 32g + r
+        float s[32];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          f32x16 st = mfma_f8(kc[t][0], qf[g][0], f32x16{}, 127, 127);
+#pragma unroll
+          for (int ks = 1; ks < KS; ++ks) st = mfma_f8(kc[t][ks], qf[g][ks], st, 127, 127);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s[16 * t + i] = st[i] * cs;
+        }
+        if (edge) {
+          const int q = qw + 32 * g + r;
+#pragma unroll
+          for (int v = 0; v < 32; ++v) {
+            const int key = kb * kRows + 32 * (v >> 4) + 8 * ((v >> 2) & 3) + 4 * hh + (v & 3);
+            if ((CAUSAL && key > q) || key >= N) s[v] = -INFINITY;
+          }
+        }
+        float mx = s[0];
+#pragma unroll
+        for (int v = 1; v < 32; ++v) mx = fmaxf(mx, s[v]);
+        mx = pair_max(mx);
+        const float m_new = fmaxf(m[g], mx);
+        if (wave_any(m_new > m[g])) {
+          const float alpha = exp2_fast(m[g] - m_new);
+          l[g] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[g][db] *= alpha;
+          m[g] = m_new;
+        }
+        float ps = 0.f;
+#pragma unroll
+        for (int v = 0; v < 32; ++v) {
+          s[v] = exp2_fast(s[v] - m[g]);
+          ps += s[v];
+        }
+        l[g] += ps;
+        // P * 2^8 as e4m3, bytes in the order of the values (V^T holds the same key order)
+        i32x8 pb;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          pb[c] = (int)cvt4_fp8(s[4 * c], s[4 * c + 1], s[4 * c + 2], s[4 * c + 3], -kPScaleLog2);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[g][db] = mfma_f8(vc[db], pb, oacc[g][db], sv, 127 - kPScaleLog2);
+      }
+    };
+    i32x8 kA[2][KS], vA[DB], kB[2][KS], vB[DB];
+    load(0, kA, vA);
+    for (int kb = 0; kb < nkb; kb += 2) {
+      step(kb, kA, vA, kB, vB);
+      if (kb + 1 < nkb) step(kb + 1, kB, vB, kA, vA);
+    }
+
+    // epilogue: O = O~ / l (bf16), LSE = (m + log2 l) ln 2
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int q = qw + 32 * g + r;
+      const float lt = pair_sum(l[g]);
+      if (q < N) {
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        uint16_t* og = p.o + (((size_t)bs * N + q) * p.heads + h) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            u32x2 wv;
+            wv[0] = pack_bf16x2(oacc[g][db][4 * i + 0] * inv, oacc[g][db][4 * i + 1] * inv);
+            wv[1] = pack_bf16x2(oacc[g][db][4 * i + 2] * inv, oacc[g][db][4 * i + 3] * inv);
+            *(u32x2*)(og + 32 * db + 8 * i + 4 * hh) = wv;
+          }
+        if (hh == 0)
+          p.lse[((size_t)bs * p.heads + h) * N + q] = lt > 0.f ? (m[g] + log2_fast(lt)) * kLn2 : -INFINITY;
+      }
+    }
+  };
+
+  // causal: workgroup p takes query blocks nb-1-p and p, so all do the same work
+  const int heavy = CAUSAL ? nb - 1 - pi : pi;
+  const int passes = CAUSAL ? (pi < heavy ? 2 : pi == heavy ? 1 : 0) : (pi < nb ? 1 : 0);
+  for (int pass = 0; pass < passes; ++pass) run_block(pass ? pi : heavy);
+}
+
+template <int D>
+hipError_t launch_d(const Fp8Args& a, hipStream_t stream) {
+  const int nblk = (a.seqlen + kRows - 1) / kRows;
+  const size_t Np = (size_t)nblk * kRows;
+  uint8_t* ws = (uint8_t*)a.workspace;
+  const Fp8Layout L = fp8_layout(a.batch, a.heads, a.kv_heads, a.seqlen, D);
+  uint8_t* q8 = ws + L.q8;
+  uint8_t* k8 = ws + L.k8;
+  uint8_t* v8t = ws + L.v8t;
+  int* eq = (int*)(ws + L.eq);
+  int* ek = (int*)(ws + L.ek);
+  int* ev = (int*)(ws + L.ev);
+  (void)Np;
+  const bool rot = a.signs != nullptr;
+  auto quant = [&](const void* x, int heads, uint8_t* out, int* exps, bool rotate, bool vt) {
+    QuantArgs qa{(const uint16_t*)x, a.signs, out, exps, heads, a.seqlen, nblk};
+    const size_t blocks = (size_t)a.batch * heads * nblk;
+    if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
+    if (vt)
+      hipLaunchKernelGGL((fp8_quant_kernel<D, false, true>), dim3((unsigned)blocks), dim3(256), 0, stream, qa);
+    else if (rotate)
+      hipLaunchKernelGGL((fp8_quant_kernel<D, true, false>), dim3((unsigned)blocks), dim3(256), 0, stream, qa);
+    else
+      hipLaunchKernelGGL((fp8_quant_kernel<D, false, false>), dim3((unsigned)blocks), dim3(256), 0, stream, qa);
+    return hipGetLastError();
+  };
+  hipError_t e;
+  if ((e = quant(a.q, a.heads, q8, eq, rot, false)) != hipSuccess) return e;
+  if ((e = quant(a.k, a.kv_heads, k8, ek, rot, false)) != hipSuccess) return e;
+  if ((e = quant(a.v, a.kv_heads, v8t, ev, false, true)) != hipSuccess) return e;
+
+  AttnArgs p;
+  p.q8 = q8;
+  p.k8 = k8;
+  p.v8t = v8t;
+  p.eq = eq;
+  p.ek = ek;
+  p.ev = ev;
+  p.o = (uint16_t*)a.o;
+  p.lse = a.lse;
+  p.heads = a.heads;
+  p.kv_heads = a.kv_heads;
+  p.group = a.heads / a.kv_heads;
+  p.seqlen = a.seqlen;
+  p.nblk = nblk;
+  const int nb = (a.seqlen + 255) / 256;
+  p.nqb = a.causal ? (nb + 1) / 2 : nb;
+  p.c2 = a.scale * kLog2e / (rot ? (float)D : 1.f);
+  const long long blocks = (long long)p.nqb * a.heads * a.batch;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (a.causal)
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, true>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, false>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+Fp8Layout fp8_layout(int B, int H, int Hkv, int N, int d) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t nblk = ((size_t)N + kRows - 1) / kRows;
+  const size_t rows_q = (size_t)B * H * nblk * kRows, rows_kv = (size_t)B * Hkv * nblk * kRows;
+  Fp8Layout L;
+  L.q8 = 0;
+  L.k8 = up(L.q8 + rows_q * d);
+  L.v8t = up(L.k8 + rows_kv * d);
+  L.eq = up(L.v8t + rows_kv * d);
+  L.ek = up(L.eq + (size_t)B * H * nblk * sizeof(int));
+  L.ev = up(L.ek + (size_t)B * Hkv * nblk * sizeof(int));
+  L.total = up(L.ev + (size_t)B * Hkv * nblk * sizeof(int));
+  return L;
+}
+
+hipError_t launch_fwd_fp8(const Fp8Args& a, hipStream_t stream) {
+  if (a.head_dim == 128) return launch_d<128>(a, stream);
+  if (a.head_dim == 64) return launch_d<64>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

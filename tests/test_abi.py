@@ -18,7 +18,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(_clib.LIB_PATH),
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_and_binding_agree():
@@ -189,6 +189,36 @@ def test_decode_paged_rejects(kw, code):
 def test_decode_paged_empty_batch_is_a_no_op():
     # B = 0 returns before touching any pointer
     assert decode_paged(B=0, q=None, kp=None, vp=None, table=None, seqlens=None, o=None, ws=None) == _clib.FA_OK
+
+
+def fwd_fp8(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, signs=None, o=FAKE, lse=FAKE, B=1, H=4, Hkv=2, N=100, d=128, scale=0.1,
+             causal=1, ws=FAKE, ws_bytes=1 << 24, stream=None)
+    a.update(kw)
+    return _clib.lib().fa_fwd_fp8(*a.values())
+
+
+def test_fwd_fp8_workspace_bytes():
+    lib = _clib.lib()
+    # B=1, H=4, Hkv=2, N=100 (two 64-row blocks), d=128: codes of Q, K, V then exponents,
+    # each part rounded up to 256 bytes
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    q8, kv8 = 4 * 128 * 128, 2 * 128 * 128
+    total = up(q8) + up(kv8) + up(kv8) + up(4 * 2 * 4) + up(2 * 2 * 4) + up(2 * 2 * 4)
+    assert lib.fa_fwd_fp8_workspace_bytes(1, 4, 2, 100, 128) == total
+    assert lib.fa_fwd_fp8_workspace_bytes(1, 4, 3, 100, 128) == 0
+    assert lib.fa_fwd_fp8_workspace_bytes(1, 4, 2, 100, 96) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hkv=3), _clib.FA_ERR_SHAPE), (dict(N=-1), _clib.FA_ERR_SHAPE), (dict(d=96), _clib.FA_ERR_HEADDIM),
+    (dict(scale=0.0), _clib.FA_ERR_ARG), (dict(causal=5), _clib.FA_ERR_ARG), (dict(q=None), _clib.FA_ERR_NULL),
+    (dict(ws=None), _clib.FA_ERR_WORKSPACE), (dict(ws_bytes=1000), _clib.FA_ERR_WORKSPACE),
+    (dict(ws=FAKE + 16), _clib.FA_ERR_ARG), (dict(signs=FAKE + 2), _clib.FA_ERR_ARG),
+    (dict(o=FAKE + 8), _clib.FA_ERR_ARG),
+])
+def test_fwd_fp8_rejects(kw, code):
+    assert fwd_fp8(**kw) == code
 
 
 def test_python_binding_refuses_cpu_tensors():

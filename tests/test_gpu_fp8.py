@@ -1,0 +1,164 @@
+"""GPU parity of fa_fwd_fp8 against the FP8 emulation in the oracle, and the page's
+accuracy claim against exact float64 attention.
+
+Quantization is integer work and is checked bit for bit: the e4m3 codes of Q, K (rotated)
+and V and every block exponent, read back from the workspace, equal the oracle's.
+
+The attention stage is floating point. The emulation forms the exponents of P as the kernel
+does (float32 scores times the kernel's float32 factor, minus the running maximum), but the
+FP8 matrix core accumulates the score products in its own order and precision (the LSE
+shows scores a few 1e-6 relative apart), so P * 2^8 near an e4m3 rounding midpoint can take
+the neighbouring code. A code moves its weight by at most one e4m3 step, 2^-3 of it, so for
+every output element |O - O_emulated| <= 2^-3 sum_j (p_j / l) |v_j| + 2^-8 |O| + 2e-3 (the
+last two terms: bf16 rounding of O, fp32 sums). Flips on large weights are rare, so at most
+5% of the rows may leave the tight bound 2^-8 |O| + 2e-3; a wrong key order, scale or layout
+moves nearly every row. LSE: within 1e-3 (unquantized sums on both sides)."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import bits_to_f64, dev_bf16, dev_f32, host
+
+pytestmark = pytest.mark.gpu
+
+
+def fa():
+    import io_aware_softmax_03_amd as m
+    return m
+
+
+def e4m3_decode(b):
+    b = np.asarray(b, dtype=np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e, m = (b >> 3) & 15, b & 7
+    return sign * np.where(e == 0, m / 8 * 2.0 ** -6, (1 + m / 8) * 2.0 ** (e - 7))
+
+
+def slot_key(s):
+    return 32 * ((s >> 4) & 1) + 8 * ((s >> 2) & 3) + 4 * (s >> 5) + (s & 3)
+
+
+def workspace_operands(ws, B, H, Hkv, N, d):
+    """Dequantized Q, K, V [B, heads, N, d] and exponents, read as include/fa.h lays them out."""
+    nb = (N + 63) // 64
+    Np = nb * 64
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    off = [0]
+    for n in (B * H * Np * d, B * Hkv * Np * d, B * Hkv * Np * d, B * H * nb * 4, B * Hkv * nb * 4):
+        off.append(up(off[-1] + n))
+    q8 = e4m3_decode(ws[off[0]:off[0] + B * H * Np * d]).reshape(B, H, Np, d)
+    k8 = e4m3_decode(ws[off[1]:off[1] + B * Hkv * Np * d]).reshape(B, Hkv, Np, d)
+    v8t = e4m3_decode(ws[off[2]:off[2] + B * Hkv * Np * d]).reshape(B, Hkv, nb, d, 64)
+    ex = [ws[o:o + n * 4].view(np.int32).reshape(B, -1, nb) for o, n in
+          ((off[3], B * H * nb), (off[4], B * Hkv * nb), (off[5], B * Hkv * nb))]
+    sc = [np.repeat(np.exp2(e.astype(np.float64)), 64, axis=2)[:, :, :N, None] for e in ex]
+    v8 = np.zeros((B, Hkv, Np, d))
+    keys = np.array([slot_key(s) for s in range(64)])
+    for blk in range(nb):
+        v8[:, :, blk * 64 + keys, :] = v8t[:, :, blk].transpose(0, 1, 3, 2)
+    return q8[:, :, :N] * sc[0], k8[:, :, :N] * sc[1], v8[:, :, :N] * sc[2], ex
+
+
+def check_row_bounds(o, o_ref, p_over_l, vabs):
+    """o, o_ref [rows, d]; p_over_l [rows, keys]; vabs [keys, d]."""
+    err = np.abs(o - o_ref)
+    loose = 2.0 ** -3 * (p_over_l @ vabs) + 2.0 ** -8 * np.abs(o_ref) + 2e-3
+    assert np.all(err <= loose), float((err - loose).max())
+    return np.any(err > 2.0 ** -8 * np.abs(o_ref) + 2e-3, axis=1)
+
+
+def weights(qh, kh, sc, causal, row0=0):
+    """Softmax weights p_j / l (float64, unquantized) of rows row0.. of one head."""
+    S = sc * (qh @ kh.T)
+    if causal:
+        S = np.where(np.arange(kh.shape[0])[None, :] <= row0 + np.arange(qh.shape[0])[:, None], S, -np.inf)
+    P = np.exp(S - S.max(axis=1, keepdims=True))
+    return P / P.sum(axis=1, keepdims=True)
+
+
+@pytest.mark.parametrize("B,N,H,Hkv,d,causal,rotate", [
+    (1, 256, 2, 2, 128, True, True),
+    (1, 256, 2, 2, 128, False, False),
+    (2, 300, 2, 1, 64, False, True),
+    (1, 700, 4, 2, 128, True, True),     # ragged last blocks, grouped heads
+    (1, 1, 1, 1, 128, True, False),
+    (1, 1000, 2, 2, 64, True, False),
+])
+def test_fwd_fp8_matches_emulation(B, N, H, Hkv, d, causal, rotate):
+    import torch
+    q = synth.outlier_tensor(41, synth.TENSOR_Q, B, N, H, d)
+    k = synth.outlier_tensor(41, synth.TENSOR_K, B, N, Hkv, d)
+    v = synth.outlier_tensor(41, synth.TENSOR_V, B, N, Hkv, d)
+    signs = synth.rademacher_signs(41, d) if rotate else None
+    ws = torch.zeros(fa().lib().fa_fwd_fp8_workspace_bytes(B, H, Hkv, N, d), dtype=torch.uint8, device="cuda")
+    o, lse = fa().fwd_fp8(dev_bf16(q), dev_bf16(k), dev_bf16(v), signs=None if signs is None else dev_f32(signs),
+                          causal=causal, workspace=ws)
+    o, lse = host(o), host(lse)
+    qg, kg, vg, _ = workspace_operands(ws.cpu().numpy(), B, H, Hkv, N, d)
+    qf, kf, vf = bits_to_f64(q), bits_to_f64(k), bits_to_f64(v)
+    c2 = oracle.kernel_score_scale_log2(1 / math.sqrt(d), d, rotate)
+    loose_rows = total_rows = 0
+    for b in range(B):
+        for h in range(H):
+            j = h // (H // Hkv)
+            qh, kh, vh, sc = oracle.fp8_operands(qf[b, :, h], kf[b, :, j], vf[b, :, j], 1 / math.sqrt(d), signs)
+            # quantization: bit-exact
+            np.testing.assert_array_equal(qg[b, h], qh)
+            np.testing.assert_array_equal(kg[b, j], kh)
+            np.testing.assert_array_equal(vg[b, j], vh)
+            o_ref, lse_ref = oracle.fp8_online_attention(qh, kh, vh, sc, causal, score_scale_log2=c2)
+            assert np.max(np.abs(lse[b, h] - lse_ref)) <= 1e-3
+            out = check_row_bounds(o[b, :, h], o_ref, weights(qh, kh, sc, causal), np.abs(vh))
+            loose_rows += int(out.sum())
+            total_rows += N
+    print(f"fp8 parity: rows outside the tight bound {loose_rows} of {total_rows}")
+    assert loose_rows <= 0.05 * total_rows
+
+
+def test_fwd_fp8_outlier_accuracy():
+    """The page's test: entries N(0,1) plus N(0,100) on 0.1% of them, d = 128. Against
+    float64 attention, rotation + block scales give an RMSE near the page's 9.1e-3 and at
+    least 1.5x below the unrotated kernel (the page: 2.4e-2 without incoherent processing)."""
+    B, N, H, d = 1, 2048, 4, 128
+    q, k, v = (synth.outlier_tensor(42, t, B, N, H, d) for t in (synth.TENSOR_Q, synth.TENSOR_K, synth.TENSOR_V))
+    exact, _ = oracle.attn_fwd(bits_to_f64(q), bits_to_f64(k), bits_to_f64(v), 1 / math.sqrt(d), False)
+    rot, _ = fa().fwd_fp8(dev_bf16(q), dev_bf16(k), dev_bf16(v), signs=dev_f32(synth.rademacher_signs(42, d)))
+    plain, _ = fa().fwd_fp8(dev_bf16(q), dev_bf16(k), dev_bf16(v))
+    rmse_rot = float(np.sqrt(np.mean((host(rot) - exact) ** 2)))
+    rmse_plain = float(np.sqrt(np.mean((host(plain) - exact) ** 2)))
+    print(f"fp8 RMSE vs float64: rotated {rmse_rot:.3e}, not rotated {rmse_plain:.3e}")
+    assert 3e-3 < rmse_rot < 1.8e-2
+    assert rmse_plain > 1.5 * rmse_rot
+
+
+def test_fwd_fp8_full_size_sampled_rows():
+    """B=2, H=16, N=8192, d=128, causal, rotated (the bench's FP8 workload): sampled rows of
+    sampled heads against the emulation (the head's operands quantized whole, the row's
+    online loop over its keys)."""
+    torch = pytest.importorskip("torch")
+    B, N, H, d = 2, 8192, 16, 128
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    q, k, v = (torch.randn((B, N, H, d), generator=gen, device="cuda", dtype=torch.bfloat16) for _ in range(3))
+    signs = synth.rademacher_signs(11, d)
+    o, lse = fa().fwd_fp8(q, k, v, signs=dev_f32(signs), causal=True)
+    o, lse = host(o), host(lse)
+    rng = np.random.default_rng(3)
+    c2 = oracle.kernel_score_scale_log2(1 / math.sqrt(d), d, True)
+    loose = total = 0
+    for b, h in ((0, 0), (1, 9)):
+        qh, kh, vh, sc = oracle.fp8_operands(host(q[b, :, h]), host(k[b, :, h]), host(v[b, :, h]), 1 / math.sqrt(d),
+                                             signs)
+        for i in sorted(set([0, 63, 64, 4095, N - 1] + list(rng.integers(0, N, 4)))):
+            o_ref, lse_ref = oracle.fp8_online_attention(qh[i:i + 1], kh[:i + 1], vh[:i + 1], sc, True, row_offset=i,
+                                                         score_scale_log2=c2)
+            out = check_row_bounds(o[b, i:i + 1, h], o_ref, weights(qh[i:i + 1], kh[:i + 1], sc, True, i),
+                                   np.abs(vh[:i + 1]))
+            loose += int(out.sum())
+            total += 1
+            assert abs(lse[b, h, i] - lse_ref[0]) <= 1e-3, (b, h, i)
+    assert loose <= max(1, 0.1 * total)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()

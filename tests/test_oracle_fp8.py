@@ -123,6 +123,21 @@ def test_unquantized_emulation_is_exact_attention(causal):
         np.testing.assert_allclose(got[1], ref[1], atol=tol)
 
 
+def test_kernel_precision_path_agrees_with_float64():
+    """The float32 base-2 formation of the exponents changes the result by float32 rounding
+    only (P unquantized), and with P quantized by at most a few flipped e4m3 codes."""
+    q, k, v = np.random.default_rng(4).standard_normal((3, 200, 64))
+    d = 64
+    ref = oracle.fp8_online_attention(q, k, v, 1 / 8, True, quantize_p=False)
+    c2 = oracle.kernel_score_scale_log2(1 / 8, d, False)
+    got = oracle.fp8_online_attention(q, k, v, 1 / 8, True, quantize_p=False, score_scale_log2=c2)
+    np.testing.assert_allclose(got[0], ref[0], atol=1e-5)
+    np.testing.assert_allclose(got[1], ref[1], atol=1e-5)
+    refq = oracle.fp8_online_attention(q, k, v, 1 / 8, True)
+    gotq = oracle.fp8_online_attention(q, k, v, 1 / 8, True, score_scale_log2=c2)
+    assert np.mean(np.abs(gotq[0] - refq[0]).max(axis=1) > 1e-5) < 0.05
+
+
 def outlier_rmse(**kw):
     B, N, H, d = 1, 1024, 2, 128
     q, k, v = (synth.f32_from_bf16_bits(synth.outlier_tensor(5, t, B, N, H, d)) for t in range(3))
