@@ -9,7 +9,8 @@ Also measured in the same run (field "extra"): the backward (B=4, H=16, N=4096, 
 causal), split-KV decode (B=64, H=32, L=32768, d=128, 64 splits), the same decode over a
 paged cache (16-token pages, lengths 16384..32768), grouped-query decode (32 query heads
 over 8 key-value heads), a chunked prefill (2048 queries on 16384 keys) and a 1024-key
-sliding window (N=8192) through the banded forward, the packed varlen
+sliding window (N=8192) through the banded forward, the FP8 forward on the headline shape,
+the packed varlen
 forward (16 sequences, H=32, d=64) and the fp32 forward (N=256, d=64); and the float64
 CPU oracle timed on a bounded sample of the headline workload (field "cpu_baseline").
 
@@ -32,6 +33,7 @@ METRIC = "attention fwd TFLOP/s (bf16 causal N=8192 d=128) and % of MFMA peak"
 # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP per clock per CU (the published 2.5 PFLOP/s)
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS  # dense e4m3 matrix-core peak (5.0 PFLOP/s)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_causal_b2_h16_n8192_d128_traffic.json")
 FWD_SOURCE = os.path.join(ROOT, "io_aware_softmax_03_amd", "csrc", "fwd_bf16.hip")
 
@@ -187,6 +189,24 @@ def extra_measurements(steps):
                      "frac_mfma_peak": round(fl / ev / 1e9 / PEAK_BF16_TFLOPS, 4),
                      "flops_convention": "4*d per visible (query, key) pair"}
         del q, k, v, o, lse
+
+    # FP8 forward on the headline shape (causal B=2 H=16 N=8192 d=128), Q and K rotated:
+    # three quantization launches plus the attention launch per call
+    B, H, N, d = 2, 16, 8192, 128
+    gen.manual_seed(11)
+    q, k, v = (torch.randn((B, N, H, d), generator=gen, device="cuda", dtype=torch.bfloat16) for _ in range(3))
+    signs = torch.from_numpy(synth.rademacher_signs(11, d)).to("cuda")
+    ws = torch.empty(fa.lib().fa_fwd_fp8_workspace_bytes(B, H, H, N, d), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    wall, ev, best = time_launches(lambda: fa.fwd_fp8(q, k, v, signs=signs, causal=True, out=(o, lse), workspace=ws),
+                                   steps, 3)
+    fl = costs.fwd_flops(B, H, N, d, True)
+    out["fwd_fp8_causal_b2_h16_n8192_d128_rotated"] = {
+        "ms": round(ev, 4), "tflops": round(fl / ev / 1e9, 2),
+        "frac_fp8_mfma_peak": round(fl / ev / 1e9 / PEAK_FP8_TFLOPS, 4),
+        "flops_convention": "4*B*H*N^2*d/2, per call (quantization of Q, K, V included)"}
+    del q, k, v, o, lse, ws
 
     # fp32 forward, B=1 H=1 N=256 d=64 (launch-latency bound)
     gen.manual_seed(1)
