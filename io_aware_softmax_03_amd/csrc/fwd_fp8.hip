@@ -12,11 +12,15 @@
 //    codes are stored head-major, [B, H, rows, d]; V codes are stored per 64-key block
 //    transposed, [B, H, block, d, 64], with the keys of a block in the order the attention
 //    kernel's P registers hold them, so each lane's V^T operand is 32 contiguous bytes.
-// 2. fwd_fp8_kernel: 4 independent waves of 64 query rows (two groups of 32) per workgroup;
-//    per 64-key block, S^T = K Q^T and O^T += V^T P^T on v_mfma_scale_f32_32x32x64_f8f6f4,
-//    the online softmax in fp32 (base 2), and P quantized to e4m3 as P * 2^8. The block
-//    scales enter exactly: 2^(eq + ek) on the score scale, 2^ev and 2^-8 through the
-//    MFMA's E8M0 operand scales. The row sum and the LSE use the unquantized P.
+// 2. fwd_fp8_kernel: 4 waves of 32 query rows per workgroup, two workgroups per CU (about
+//    200 registers a wave), so one wave's softmax runs beside another's matrix-core work.
+//    Per 64-key block the K and V^T tiles (contiguous 8 KB blocks of the workspace) are
+//    copied straight into LDS one block ahead and shared by the four waves; S^T = K Q^T
+//    and O^T += V^T P^T run on v_mfma_scale_f32_32x32x64_f8f6f4, the online softmax in
+//    fp32 (base 2), and P is quantized to e4m3 as P * 2^8 (formed directly as
+//    2^(s - m + 8)). The block scales enter exactly: 2^(eq + ek) on the score scale, 2^ev and
+//    2^-8 through the MFMA's E8M0 operand scales. The row sum and the LSE use the
+//    unquantized P.
 //
 // Operand layouts of v_mfma_scale_f32_32x32x64_f8f6f4 with e4m3 operands (lane l, r = l%32,
 // hh = l/32): A row r, B column r; the 32 bytes of a lane are 32 of the 64 k indices, and A
@@ -185,22 +189,41 @@ __device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, const 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
+// LDS tiles of one 64-key block, filled by buffer loads straight into LDS. 16-byte chunks are
+// XOR-swizzled by row so that the 16 lanes of each quarter-wave read hit 16 distinct bank
+// groups: K rows (128 bytes, 8 chunks) by (row / 2) % 8; V^T rows (64 bytes, 4 chunks, one
+// row per head dim) by (row / 4) % 4.
+template <int D>
+__device__ __forceinline__ int swz_kt(int row) { return D == 128 ? ((row >> 1) & 7) : ((row >> 2) & 3); }
+__device__ __forceinline__ int swz_vt8(int row) { return (row >> 2) & 3; }
+
+constexpr int kQRows = 128;  // query rows per workgroup: 4 waves x 32
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void fwd_fp8_kernel(AttnArgs p) {
-  constexpr int KS = D / 64;  // k-steps of S^T over the head dim
-  constexpr int DB = D / 32;  // 32-dim blocks of O^T
-  constexpr int QB = 256;     // query rows per workgroup
+__global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(AttnArgs p) {
+  constexpr int KS = D / 64;          // k-steps of S^T over the head dim
+  constexpr int DB = D / 32;          // 32-dim blocks of O^T
+  constexpr int TILE = kRows * D;     // bytes of one K block or one V^T block
+  constexpr int LOADS = TILE / 1024 / 4;  // 1 KB wave-loads per wave per tile
+  static_assert(TILE % 4096 == 0, "tile must split over four waves");
+  __shared__ __attribute__((aligned(1024))) char k_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[TILE];
+  auto kbuf = [&](auto bc) -> char* { return (decltype(bc)::value & 1) ? k_lds1 : k_lds0; };
+  auto vbuf = [&](auto bc) -> char* { return (decltype(bc)::value & 1) ? v_lds1 : v_lds0; };
+
   const int w = group_id_x();
   const int pi = w % p.nqb;
   const int bh = w / p.nqb;
   const int h = bh % p.heads, bs = bh / p.heads;
   const int hk = h / p.group;
   const int N = p.seqlen;
-  const int nb = (N + QB - 1) / QB;
+  const int nb = (N + kQRows - 1) / kQRows;
   const size_t Np = (size_t)p.nblk * kRows;
-  const size_t qbase = ((size_t)bs * p.heads + h) * Np;   // row index of the head's first row
-  const size_t kbase = ((size_t)bs * p.kv_heads + hk) * Np;
-  const size_t vblk0 = ((size_t)bs * p.kv_heads + hk) * p.nblk;
+  const uint8_t* qhead = p.q8 + ((size_t)bs * p.heads + h) * Np * D;
+  const uint8_t* khead = p.k8 + ((size_t)bs * p.kv_heads + hk) * Np * D;
+  const uint8_t* vhead = p.v8t + ((size_t)bs * p.kv_heads + hk) * Np * D;
   const int* __restrict__ ekp = p.ek + ((size_t)bs * p.kv_heads + hk) * p.nblk;
   const int* __restrict__ evp = p.ev + ((size_t)bs * p.kv_heads + hk) * p.nblk;
 
@@ -208,129 +231,167 @@ __global__ __launch_bounds__(256, 1) void fwd_fp8_kernel(AttnArgs p) {
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, r = lane & 31, hh = lane >> 5;
 
-  auto run_block = [&](int qb) {
-    const int qw = qb * QB + 64 * wid;  // this wave's first row
-    if (qw >= N) return;
-    const int eq = p.eq[((size_t)bs * p.heads + h) * p.nblk + qw / kRows];
-    // Q^T operands: query qw + 32g + r, dims 64ks + 32hh .. +31
-    i32x8 qf[2][KS];
+  // per-lane source offsets of this wave's wave-loads (the lane fetches the logical chunk
+  // the swizzle puts at its physical place) and LDS read offsets of the operands
+  unsigned k_src[LOADS], v_src[LOADS];
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+  for (int it = 0; it < LOADS; ++it) {
+    const int byte = (wid * LOADS + it) * 1024 + 16 * lane;  // physical byte in the tile
+    const int kr = byte / (D), kp = (byte % D) / 16;
+    k_src[it] = (unsigned)(kr * D + ((kp ^ swz_kt<D>(kr)) * 16));
+    const int vr = byte / kRows, vp = (byte % kRows) / 16;
+    v_src[it] = (unsigned)(vr * kRows + ((vp ^ swz_vt8(vr)) * 16));
+  }
+  int k_off[2][KS][2], v_off[DB][2];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        qf[g][ks] = *(const i32x8*)(p.q8 + (qbase + qw + 32 * g + r) * D + 64 * ks + 32 * hh);
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int row = 32 * t + r, chunk = 4 * ks + 2 * hh + c;
+        k_off[t][ks][c] = row * D + ((chunk ^ swz_kt<D>(row)) * 16);
+      }
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int row = 32 * db + r, chunk = 2 * hh + c;
+      v_off[db][c] = row * kRows + ((chunk ^ swz_vt8(row)) * 16);
+    }
 
-    const int nkb = CAUSAL ? qw / kRows + 1 : p.nblk;
-    auto load = [&](int kb, i32x8 (&kd)[2][KS], i32x8 (&vd)[DB]) {
+  auto run_block = [&](int qb) {
+    const int q0 = qb * kQRows;
+    const int qw = q0 + 32 * wid;  // this wave's 32 rows
+    const bool active = qw < N;
+    // key blocks of the workgroup (all waves load and wait on them) and of this wave
+    const int nkb = CAUSAL ? min(p.nblk, (min(q0 + kQRows, N) - 1) / kRows + 1) : p.nblk;
+    const int nkw = !active ? 0 : CAUSAL ? (qw + 31) / kRows + 1 : p.nblk;
+    const int eq = active ? p.eq[((size_t)bs * p.heads + h) * p.nblk + qw / kRows] : 0;
+    i32x8 qf[KS];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = active ? *(const i32x8*)(qhead + (size_t)(qw + r) * D + 64 * ks + 32 * hh) : i32x8{};
+
+    auto issue = [&](auto bufc, int kb) {
+      const __amdgpu_buffer_rsrc_t ks_ = make_rsrc(khead + (size_t)kb * TILE, TILE);
+      const __amdgpu_buffer_rsrc_t vs_ = make_rsrc(vhead + (size_t)kb * TILE, TILE);
+      char* kd = kbuf(bufc) + wid * LOADS * 1024;
+      char* vd = vbuf(bufc) + wid * LOADS * 1024;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          kd[t][ks] = *(const i32x8*)(p.k8 + (kbase + (size_t)kb * kRows + 32 * t + r) * D + 64 * ks + 32 * hh);
+      for (int it = 0; it < LOADS; ++it) copy16_to_lds(ks_, k_src[it], kd + it * 1024);
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        vd[db] = *(const i32x8*)(p.v8t + ((vblk0 + kb) * D + 32 * db + r) * kRows + 32 * hh);
+      for (int it = 0; it < LOADS; ++it) copy16_to_lds(vs_, v_src[it], vd + it * 1024);
+    };
+    auto read8 = [](const char* base, int o0, int o1) {
+      const u32x4 a = *(const u32x4*)(base + o0);
+      const u32x4 b = *(const u32x4*)(base + o1);
+      return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
     };
 
-    float m[2] = {-1e30f, -1e30f}, l[2] = {0.f, 0.f};
-    f32x16 oacc[2][DB];
+    float m = -1e30f, l = 0.f;
+    f32x16 oacc[DB];
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[g][db][i] = 0.f;
+      for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
 
-    // one 64-key block from operands kc, vc, with the next block's loads into kn, vn first
-    auto step = [&](int kb, const i32x8 (&kc)[2][KS], const i32x8 (&vc)[DB], i32x8 (&kn)[2][KS],
-                    i32x8 (&vn)[DB]) {
-      if (kb + 1 < nkb) load(kb + 1, kn, vn);
+    auto compute = [&](auto bufc, int kb) {
+      const char* kb_ = kbuf(bufc);
+      const char* vb_ = vbuf(bufc);
       const float cs = __builtin_amdgcn_ldexpf(p.c2, eq + ekp[kb]);
       const int sv = evp[kb] + 127;
-      // edge block: the causal diagonal or the ragged end
-      const bool edge = (CAUSAL && kb * kRows + kRows - 1 > qw) || (kb * kRows + kRows > N);
+      // value 16t + 4i + j: score of key kb*64 + 32t + 8i + 4hh + j, query qw + r
+      float s[32];
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        // value 16t + 4i + j: score of key kb*64 + 32t + 8i + 4hh + j, query qw + 32g + r
-        float s[32];
+      for (int t = 0; t < 2; ++t) {
+        f32x16 st = mfma_f8(read8(kb_, k_off[t][0][0], k_off[t][0][1]), qf[0], f32x16{}, 127, 127);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          f32x16 st = mfma_f8(kc[t][0], qf[g][0], f32x16{}, 127, 127);
+        for (int ks = 1; ks < KS; ++ks)
+          st = mfma_f8(read8(kb_, k_off[t][ks][0], k_off[t][ks][1]), qf[ks], st, 127, 127);
 #pragma unroll
-          for (int ks = 1; ks < KS; ++ks) st = mfma_f8(kc[t][ks], qf[g][ks], st, 127, 127);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) s[16 * t + i] = st[i] * cs;
-        }
-        if (edge) {
-          const int q = qw + 32 * g + r;
-#pragma unroll
-          for (int v = 0; v < 32; ++v) {
-            const int key = kb * kRows + 32 * (v >> 4) + 8 * ((v >> 2) & 3) + 4 * hh + (v & 3);
-            if ((CAUSAL && key > q) || key >= N) s[v] = -INFINITY;
-          }
-        }
-        float mx = s[0];
-#pragma unroll
-        for (int v = 1; v < 32; ++v) mx = fmaxf(mx, s[v]);
-        mx = pair_max(mx);
-        const float m_new = fmaxf(m[g], mx);
-        if (wave_any(m_new > m[g])) {
-          const float alpha = exp2_fast(m[g] - m_new);
-          l[g] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) oacc[g][db] *= alpha;
-          m[g] = m_new;
-        }
-        float ps = 0.f;
+        for (int i = 0; i < 16; ++i) s[16 * t + i] = st[i];
+      }
+      if ((CAUSAL && kb * kRows + kRows - 1 > qw) || kb * kRows + kRows > N) {
+        const int q = qw + r;
 #pragma unroll
         for (int v = 0; v < 32; ++v) {
-          s[v] = exp2_fast(s[v] - m[g]);
-          ps += s[v];
+          const int key = kb * kRows + 32 * (v >> 4) + 8 * ((v >> 2) & 3) + 4 * hh + (v & 3);
+          if ((CAUSAL && key > q) || key >= N) s[v] = -INFINITY;
         }
-        l[g] += ps;
-        // P * 2^8 as e4m3, bytes in the order of the values (V^T holds the same key order)
-        i32x8 pb;
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-          pb[c] = (int)cvt4_fp8(s[4 * c], s[4 * c + 1], s[4 * c + 2], s[4 * c + 3], -kPScaleLog2);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[g][db] = mfma_f8(vc[db], pb, oacc[g][db], sv, 127 - kPScaleLog2);
       }
+      // the scale is positive: the maximum of the raw scores gives that of the scaled ones
+      float mx = s[0];
+#pragma unroll
+      for (int v = 1; v < 32; ++v) mx = fmaxf(mx, s[v]);
+      mx = pair_max(mx) * cs;
+      const float m_new = fmaxf(m, mx);
+      if (wave_any(m_new > m)) {
+        const float alpha = exp2_fast(m - m_new);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        m = m_new;
+      }
+      // P * 2^8 directly: 2^(s cs - m + 8); the row sum takes P = that * 2^-8
+      const float mm = m - (float)kPScaleLog2;
+      float ps = 0.f;
+#pragma unroll
+      for (int v = 0; v < 32; ++v) {
+        s[v] = exp2_fast(__builtin_fmaf(s[v], cs, -mm));
+        ps += s[v];
+      }
+      l = __builtin_fmaf(ps, 1.0f / (1 << kPScaleLog2), l);
+      i32x8 pb;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) pb[c] = (int)cvt4_fp8(s[4 * c], s[4 * c + 1], s[4 * c + 2], s[4 * c + 3], 0);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        oacc[db] = mfma_f8(read8(vb_, v_off[db][0], v_off[db][1]), pb, oacc[db], sv, 127 - kPScaleLog2);
     };
-    i32x8 kA[2][KS], vA[DB], kB[2][KS], vB[DB];
-    load(0, kA, vA);
+
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    auto step = [&](auto bufc, int kb) {
+      if (kb + 1 < nkb) issue(std::integral_constant<int, decltype(bufc)::value ^ 1>(), kb + 1);
+      if (kb < nkw) compute(bufc, kb);
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of block kb + 1 have landed
+      __syncthreads();                // ... and everyone's; block kb is free for reuse
+    };
+    issue(B0(), 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
     for (int kb = 0; kb < nkb; kb += 2) {
-      step(kb, kA, vA, kB, vB);
-      if (kb + 1 < nkb) step(kb + 1, kB, vB, kA, vA);
+      step(B0(), kb);
+      if (kb + 1 < nkb) step(B1(), kb + 1);
     }
 
     // epilogue: O = O~ / l (bf16), LSE = (m + log2 l) ln 2
+    const int q = qw + r;
+    const float lt = pair_sum(l);
+    if (active && q < N) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      uint16_t* og = p.o + (((size_t)bs * N + q) * p.heads + h) * D;
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const int q = qw + 32 * g + r;
-      const float lt = pair_sum(l[g]);
-      if (q < N) {
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        uint16_t* og = p.o + (((size_t)bs * N + q) * p.heads + h) * D;
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            u32x2 wv;
-            wv[0] = pack_bf16x2(oacc[g][db][4 * i + 0] * inv, oacc[g][db][4 * i + 1] * inv);
-            wv[1] = pack_bf16x2(oacc[g][db][4 * i + 2] * inv, oacc[g][db][4 * i + 3] * inv);
-            *(u32x2*)(og + 32 * db + 8 * i + 4 * hh) = wv;
-          }
-        if (hh == 0)
-          p.lse[((size_t)bs * p.heads + h) * N + q] = lt > 0.f ? (m[g] + log2_fast(lt)) * kLn2 : -INFINITY;
-      }
+        for (int i = 0; i < 4; ++i) {
+          u32x2 wv;
+          wv[0] = pack_bf16x2(oacc[db][4 * i + 0] * inv, oacc[db][4 * i + 1] * inv);
+          wv[1] = pack_bf16x2(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv);
+          *(u32x2*)(og + 32 * db + 8 * i + 4 * hh) = wv;
+        }
+      if (hh == 0) p.lse[((size_t)bs * p.heads + h) * N + q] = lt > 0.f ? (m + log2_fast(lt)) * kLn2 : -INFINITY;
     }
   };
 
   // causal: workgroup p takes query blocks nb-1-p and p, so all do the same work
   const int heavy = CAUSAL ? nb - 1 - pi : pi;
   const int passes = CAUSAL ? (pi < heavy ? 2 : pi == heavy ? 1 : 0) : (pi < nb ? 1 : 0);
-  for (int pass = 0; pass < passes; ++pass) run_block(pass ? pi : heavy);
+  for (int pass = 0; pass < passes; ++pass) {
+    if (pass) __syncthreads();  // every wave is done with the first block's tiles
+    run_block(pass ? pi : heavy);
+  }
 }
 
 template <int D>
@@ -378,7 +439,7 @@ hipError_t launch_d(const Fp8Args& a, hipStream_t stream) {
   p.group = a.heads / a.kv_heads;
   p.seqlen = a.seqlen;
   p.nblk = nblk;
-  const int nb = (a.seqlen + 255) / 256;
+  const int nb = (a.seqlen + kQRows - 1) / kQRows;
   p.nqb = a.causal ? (nb + 1) / 2 : nb;
   p.c2 = a.scale * kLog2e / (rot ? (float)D : 1.f);
   const long long blocks = (long long)p.nqb * a.heads * a.batch;
