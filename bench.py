@@ -117,7 +117,7 @@ def cpu_baseline(target_s):
     N, d = 8192, 128
     scale = 1 / math.sqrt(d)
     heads, elapsed = 0, 0.0
-    while elapsed < target_s and heads < 16:
+    while elapsed < target_s and heads < 32:
         b, h = divmod(heads, 16)
         qkv = [synth.f32_from_bf16_bits(synth.bf16_bits_from_f32(synth.normal_slice(2, t, b, h, (N, d))))
                .astype(np.float64) for t in (synth.TENSOR_Q, synth.TENSOR_K, synth.TENSOR_V)]

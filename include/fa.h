@@ -166,7 +166,7 @@ size_t fa_fwd_fp8_workspace_bytes(int B, int H, int Hkv, int N, int d);
  * section "FP8, and the outlier problem"), same inputs and outputs as fa_fwd with
  * dtype FA_DTYPE_BF16:
  *   q [B, N, H, d], k, v [B, N, Hkv, d] bf16; o [B, N, H, d] bf16; lse fp32 [B, H, N]
- *   signs     device fp32 [d] of +1/-1, or NULL. Given, Q and K are first rotated by
+ *   signs     device fp32 [d] of +1/-1 (16-byte aligned), or NULL. Given, Q and K are rotated by
  *             R = H_d diag(signs) / sqrt(d) (incoherent processing: the scores are
  *             unchanged in exact arithmetic, outliers are spread over all coordinates).
  *   Each block of 64 rows of one head of Q, K and V gets its own power-of-two scale

@@ -160,7 +160,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, const float* signs, 
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (!workspace || workspace_bytes < fa_fwd_fp8_workspace_bytes(B, H, Hkv, N, d)) return FA_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
-      ((uintptr_t)workspace & 255u) != 0 || ((uintptr_t)signs & 3u) != 0)
+      ((uintptr_t)workspace & 255u) != 0 || ((uintptr_t)signs & 15u) != 0)
     return FA_ERR_ARG;
   fa::Fp8Args a{q, k, v, signs, o, lse, workspace, B, H, Hkv, N, d, scale, causal != 0};
   return from_hip(fa::launch_fwd_fp8(a, (hipStream_t)stream));

@@ -60,6 +60,13 @@ __device__ __forceinline__ int slot_key(int s) {
   return 32 * t + 8 * i + 4 * hh + j;
 }
 
+// value of lane l ^ M within each group of four lanes (DPP quad permutation)
+template <int M>
+__device__ __forceinline__ float quad_xor(float x) {
+  constexpr int ctrl = M == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xf, 0xf, false));
+}
+
 template <int D, bool ROTATE, bool VT>
 __global__ __launch_bounds__(256) void fp8_quant_kernel(QuantArgs p) {
   constexpr int EPT = D / 4;  // elements per thread: each row is spread over 4 threads
@@ -90,9 +97,19 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(QuantArgs p) {
     for (int i = 0; i < EPT; ++i) y[i] = 0.f;
   }
 
+  float sg[ROTATE ? EPT : 1];
+  if constexpr (ROTATE) {
+#pragma unroll
+    for (int c = 0; c < EPT / 4; ++c) {
+      const f32x4 v = *(const f32x4*)(p.signs + part * EPT + 4 * c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sg[4 * c + e] = v[e];
+    }
+  }
+
   if constexpr (ROTATE) {
     // x H_d: butterflies (a, b) -> (a + b, a - b), strides 1 .. EPT/2 inside the thread,
-    // then EPT and 2 EPT between the row's four threads (adjacent lanes)
+    // then EPT and 2 EPT between the row's four threads (adjacent lanes of a quad)
 #pragma unroll
     for (int hs = 1; hs < EPT; hs <<= 1)
 #pragma unroll
@@ -102,17 +119,24 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(QuantArgs p) {
           y[i] = a + c;
           y[i + hs] = a - c;
         }
-#pragma unroll
-    for (int m = 1; m < 4; m <<= 1) {
-      const bool upper = (part & m) != 0;
+    {
+      const bool upper = (part & 1) != 0;
 #pragma unroll
       for (int i = 0; i < EPT; ++i) {
-        const float o = __shfl_xor(y[i], m);
+        const float o = quad_xor<1>(y[i]);
+        y[i] = upper ? o - y[i] : y[i] + o;
+      }
+    }
+    {
+      const bool upper = (part & 2) != 0;
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        const float o = quad_xor<2>(y[i]);
         y[i] = upper ? o - y[i] : y[i] + o;
       }
     }
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) y[i] *= p.signs[part * EPT + i];
+    for (int i = 0; i < EPT; ++i) y[i] *= sg[i];
   }
 
   // block maximum magnitude -> exponent: smallest e with amax <= 448 * 2^e
@@ -152,22 +176,27 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(QuantArgs p) {
       *(u32x4*)(tile + r * D + part * EPT + 16 * c) = v;
     }
     __syncthreads();
-    constexpr int BPT = D * kRows / 256;  // bytes per thread: 32 (D = 128) or 16 (D = 64)
-    const int o0 = t * BPT;
-    const int dim = o0 / kRows, s0 = o0 % kRows;
-    uint32_t wv[BPT / 4];
+    // 4 x 4 byte blocks: slots 4sg .. 4sg+3 (four consecutive keys from slot_key(4sg)) of
+    // dims 4dg .. 4dg+3; one 4-byte LDS read per key, a byte transpose, one 4-byte store per
+    // dim (16 consecutive threads fill a dim's 64 bytes)
+    uint8_t* dst = p.out + ((size_t)bh * p.nblk + blk) * D * kRows;
+    constexpr int GROUPS = (D / 4) * (kRows / 4);
 #pragma unroll
-    for (int i = 0; i < BPT / 4; ++i) {
-      uint32_t x = 0;
+    for (int g = t; g < GROUPS; g += 256) {
+      const int dg = g / (kRows / 4), sg = g % (kRows / 4);
+      const int k0 = slot_key(4 * sg);
+      uint32_t wk[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x |= (uint32_t)tile[slot_key(s0 + 4 * i + j) * D + dim] << (8 * j);
-      wv[i] = x;
-    }
-    uint8_t* dst = p.out + ((size_t)bh * p.nblk + blk) * D * kRows + o0;
+      for (int j = 0; j < 4; ++j) wk[j] = *(const uint32_t*)(tile + (k0 + j) * D + 4 * dg);
+      // v_perm_b32(a, b, sel): selector bytes 0-3 pick bytes of b, 4-7 bytes of a
+      const uint32_t t0 = __builtin_amdgcn_perm(wk[1], wk[0], 0x05010400u);
+      const uint32_t t1 = __builtin_amdgcn_perm(wk[1], wk[0], 0x07030602u);
+      const uint32_t t2 = __builtin_amdgcn_perm(wk[3], wk[2], 0x05010400u);
+      const uint32_t t3 = __builtin_amdgcn_perm(wk[3], wk[2], 0x07030602u);
+      const uint32_t od[4] = {__builtin_amdgcn_perm(t2, t0, 0x05040100u), __builtin_amdgcn_perm(t2, t0, 0x07060302u),
+                              __builtin_amdgcn_perm(t3, t1, 0x05040100u), __builtin_amdgcn_perm(t3, t1, 0x07060302u)};
 #pragma unroll
-    for (int c = 0; c < BPT / 16; ++c) {
-      u32x4 v = {wv[4 * c], wv[4 * c + 1], wv[4 * c + 2], wv[4 * c + 3]};
-      *(u32x4*)(dst + 16 * c) = v;
+      for (int e = 0; e < 4; ++e) *(uint32_t*)(dst + (4 * dg + e) * kRows + 4 * sg) = od[e];
     }
   }
 }

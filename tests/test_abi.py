@@ -214,7 +214,7 @@ def test_fwd_fp8_workspace_bytes():
     (dict(Hkv=3), _clib.FA_ERR_SHAPE), (dict(N=-1), _clib.FA_ERR_SHAPE), (dict(d=96), _clib.FA_ERR_HEADDIM),
     (dict(scale=0.0), _clib.FA_ERR_ARG), (dict(causal=5), _clib.FA_ERR_ARG), (dict(q=None), _clib.FA_ERR_NULL),
     (dict(ws=None), _clib.FA_ERR_WORKSPACE), (dict(ws_bytes=1000), _clib.FA_ERR_WORKSPACE),
-    (dict(ws=FAKE + 16), _clib.FA_ERR_ARG), (dict(signs=FAKE + 2), _clib.FA_ERR_ARG),
+    (dict(ws=FAKE + 16), _clib.FA_ERR_ARG), (dict(signs=FAKE + 2), _clib.FA_ERR_ARG), (dict(signs=FAKE + 4), _clib.FA_ERR_ARG),
     (dict(o=FAKE + 8), _clib.FA_ERR_ARG),
 ])
 def test_fwd_fp8_rejects(kw, code):
