@@ -233,26 +233,29 @@ def extra_measurements(steps):
     del q, kc, vc, ws
     torch.cuda.empty_cache()
 
-    # grouped-query decode: 32 query heads over 8 key-value heads, otherwise as above
+    # grouped-query decode: 32 query heads over 8 key-value heads, L=32768, d=128; 32 splits
+    # (a sweep over 16..256 puts the grouped kernel's best at 32: with 8 key-value heads a
+    # 64-way split leaves each wave only 512 keys)
     B, H, Hkv, L, d = 64, 32, 8, 32768, 128
     gen.manual_seed(9)
     q = torch.randn((B, H, d), generator=gen, device="cuda", dtype=torch.bfloat16)
     kc = torch.randn((B, L, Hkv, d), generator=gen, device="cuda", dtype=torch.bfloat16)
     vc = torch.randn((B, L, Hkv, d), generator=gen, device="cuda", dtype=torch.bfloat16)
-    ws = torch.empty(fa.lib().fa_decode_workspace_bytes(B, H, d, 64), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(fa.lib().fa_decode_workspace_bytes(B, H, d, 32), dtype=torch.uint8, device="cuda")
     o = torch.empty_like(q)
     lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
-    wall, ev, best = time_launches(lambda: fa.decode(q, kc, vc, num_splits=64, workspace=ws, out=(o, lse)),
+    wall, ev, best = time_launches(lambda: fa.decode(q, kc, vc, num_splits=32, workspace=ws, out=(o, lse)),
                                    max(3, steps // 2), 2)
     nb = costs.decode_bytes(B, Hkv, L, d) + 2.0 * B * (H - Hkv) * d * 2
-    out["decode_gqa_b64_h32_kv8_l32768_d128_s64"] = {
+    out["decode_gqa_b64_h32_kv8_l32768_d128_s32"] = {
         "ms": round(ev, 4), "gbs": round(nb / ev / 1e6, 1), "frac_hbm_peak": round(nb / ev / 1e6 / PEAK_HBM_GBS, 4),
         "bytes_convention": "K and V caches (8 heads) read once + q + o (32 heads)"}
     del q, kc, vc, ws
     torch.cuda.empty_cache()
 
     # paged decode: B=64 H=32 d=128, 16-token pages scattered over the pool, lengths uniform
-    # in [16384, 32768], 64 splits
+    # in [16384, 32768], 32 splits (the sweep's best; sequences are up to half as long as
+    # the contiguous decode's)
     B, H, d, P = 64, 32, 128, 16
     seqlens = synth.varlen_lengths(8, B, 16384, 32768).tolist()
     table, num_pages = synth.paged_layout(8, seqlens, P, 0)
@@ -262,14 +265,14 @@ def extra_measurements(steps):
     vp = torch.randn((num_pages, P, H, d), generator=gen, device="cuda", dtype=torch.bfloat16)
     tab = torch.from_numpy(table).to("cuda")
     sl = torch.tensor(seqlens, dtype=torch.int32, device="cuda")
-    ws = torch.empty(fa.lib().fa_decode_workspace_bytes(B, H, d, 64), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(fa.lib().fa_decode_workspace_bytes(B, H, d, 32), dtype=torch.uint8, device="cuda")
     o = torch.empty_like(q)
     lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
     wall, ev, best = time_launches(
-        lambda: fa.decode_paged(q, kp, vp, tab, sl, num_splits=64, workspace=ws, out=(o, lse)),
+        lambda: fa.decode_paged(q, kp, vp, tab, sl, num_splits=32, workspace=ws, out=(o, lse)),
         max(3, steps // 2), 2)
     nb = costs.decode_paged_bytes(seqlens, H, d)
-    out["decode_paged_b64_h32_p16_l16k_32k_d128_s64"] = {
+    out["decode_paged_b64_h32_p16_l16k_32k_d128_s32"] = {
         "ms": round(ev, 4), "gbs": round(nb / ev / 1e6, 1), "frac_hbm_peak": round(nb / ev / 1e6 / PEAK_HBM_GBS, 4),
         "tokens": int(sum(seqlens)), "bytes_convention": "valid K and V tokens read once + q + o"}
     del q, kp, vp, ws
@@ -352,6 +355,16 @@ def main():
         "device": {"name": prop.name, "gcn_arch": getattr(prop, "gcnArchName", ""),
                    "cus": prop.multi_processor_count, "clocks_during_headline": clocks},
     }
+    # the same fraction against the dense bf16 peak at the shader clock read during the run
+    # (256 CUs x 4096 FLOP per clock): the published peak assumes 2.4 GHz
+    try:
+        sclk = float(clocks["sclk_mhz"]) if clocks else None
+    except (KeyError, TypeError, ValueError):
+        sclk = None
+    if sclk:
+        peak_at_clock = prop.multi_processor_count * 4096 * sclk * 1e6 / 1e12
+        result["roofline"]["peak_at_measured_sclk"] = round(peak_at_clock, 1)
+        result["roofline"]["frac_at_measured_sclk"] = round(achieved / peak_at_clock, 4)
     del q, k, v, o, lse
     torch.cuda.empty_cache()
     if not args.no_extra:
