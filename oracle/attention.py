@@ -33,7 +33,8 @@ Readings taken where the pages are silent (each is listed in the design notes):
   fewer key-value heads than query heads, shared in groups without copying K
   and V): with H query heads and Hkv key-value heads, the query heads form Hkv
   consecutive groups of H / Hkv and group j reads key-value head j. Hkv = H is
-  ordinary multi-head attention.
+  ordinary multi-head attention. In the backward a shared key-value head gets the sum of
+  its group's gradients.
 * the backward pass is the exact gradient of O(q, k, v) for an upstream dO,
   derived by calculus from the definition above; the pages state only that it
   recomputes the tiles from the saved LSE.
@@ -183,16 +184,21 @@ def attn_bwd_head(q, k, v, do, scale, causal=False):
 
 
 def attn_bwd(q, k, v, do, scale, causal=False):
-    """Dense backward. All tensors [B, N, H, d]; returns (dq, dk, dv) in float64."""
+    """Dense backward. q, do: [B, N, H, d]; k, v: [B, N, Hkv, d] (grouped as in attn_fwd).
+    Returns (dq [B, N, H, d], dk, dv [B, N, Hkv, d]) in float64. A key-value head shared by
+    a group of query heads receives the sum of the group's gradients (the chain rule through
+    every use of it)."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     B, N, H, _ = q.shape
-    if k.shape[2] != H:
-        raise ValueError("the backward is defined here for multi-head attention only (Hkv = H)")
-    dq, dk, dv = np.empty(q.shape), np.empty(k.shape), np.empty(v.shape)
+    Hkv = k.shape[2]
+    dq, dk, dv = np.empty(q.shape), np.zeros(k.shape), np.zeros(v.shape)
     for b in range(B):
         for h in range(H):
-            g = attn_bwd_head(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], scale, causal)
-            dq[b, :, h], dk[b, :, h], dv[b, :, h] = g["dq"], g["dk"], g["dv"]
+            j = kv_head(h, H, Hkv)
+            g = attn_bwd_head(q[b, :, h], k[b, :, j], v[b, :, j], do[b, :, h], scale, causal)
+            dq[b, :, h] = g["dq"]
+            dk[b, :, j] += g["dk"]
+            dv[b, :, j] += g["dv"]
     return dq, dk, dv
 
 

@@ -103,7 +103,50 @@ def test_heads_must_divide():
     with pytest.raises(ValueError):
         oracle.attn_fwd(q, k, k, 0.5)
     with pytest.raises(ValueError):
-        oracle.attn_bwd(q, k, k, q, 0.5)   # the backward is multi-head only
+        oracle.attn_bwd(q, k, k, q, 0.5)
+
+
+def _grouped_loss(q, k, v, do, scale, causal):
+    """sum(O * dO) of the grouped forward, through the scalar brute force per query head."""
+    from oracle.algorithms import brute_force_attention
+    H, Hkv = q.shape[2], k.shape[2]
+    total = 0.0
+    for h in range(H):
+        j = h // (H // Hkv)
+        o, _ = brute_force_attention(q[0, :, h], k[0, :, j], v[0, :, j], scale, causal)
+        total += float(np.sum(np.asarray(o) * do[0, :, h]))
+    return total
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_backward_finite_differences(causal):
+    """dK, dV of a shared head by central differences of sum(O * dO) through the scalar
+    brute force: the shared head's gradient is the sum over its group."""
+    B, N, H, Hkv, d, scale, step = 1, 5, 4, 2, 3, 0.7, 1e-6
+    q, k, v, do = rand(30, B, N, H, d), rand(31, B, N, Hkv, d), rand(32, B, N, Hkv, d), rand(33, B, N, H, d)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, scale, causal)
+    for name, x, g in (("k", k, dk), ("v", v, dv), ("q", q, dq)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += step
+            xm[idx] -= step
+            args_p, args_m = {"q": q, "k": k, "v": v}, {"q": q, "k": k, "v": v}
+            args_p[name], args_m[name] = xp, xm
+            num[idx] = (_grouped_loss(args_p["q"], args_p["k"], args_p["v"], do, scale, causal)
+                        - _grouped_loss(args_m["q"], args_m["k"], args_m["v"], do, scale, causal)) / (2 * step)
+        assert np.max(np.abs(g - num)) / max(1.0, np.max(np.abs(num))) <= 1e-6, name
+
+
+def test_grouped_backward_is_multi_head_on_repeated_heads_summed():
+    B, N, H, Hkv, d = 2, 7, 6, 3, 4
+    q, k, v, do = rand(34, B, N, H, d), rand(35, B, N, Hkv, d), rand(36, B, N, Hkv, d), rand(37, B, N, H, d)
+    g = H // Hkv
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, 0.4, True)
+    dq2, dk2, dv2 = oracle.attn_bwd(q, np.repeat(k, g, axis=2), np.repeat(v, g, axis=2), do, 0.4, True)
+    np.testing.assert_allclose(dq, dq2, atol=1e-13)
+    np.testing.assert_allclose(dk, dk2.reshape(B, N, Hkv, g, d).sum(axis=3), atol=1e-13)
+    np.testing.assert_allclose(dv, dv2.reshape(B, N, Hkv, g, d).sum(axis=3), atol=1e-13)
 
 
 def _fwd_interleaved(q, k, v, scale, causal=False):
