@@ -25,7 +25,7 @@
  *            shared in groups without copying K and V). Query heads form Hkv
  *            consecutive groups of H / Hkv; group j reads key-value head j. K
  *            and V then have Hkv in place of H in their shapes. Hkv = H is
- *            ordinary multi-head attention; fa_bwd is multi-head only.
+ *            ordinary multi-head attention.
  *   Causal   query i sees key j when j <= i, both counted from the start of
  *            the sequence. For the square shapes accepted here this is both the
  *            top-left and the bottom-right alignment described in
@@ -140,20 +140,25 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N);
  * fa_bwd — backward by recomputation ("FlashAttention: IO-aware exact
  * attention", "Tile decomposition", last paragraph; "FlashAttention-2 and -3",
  * "Parallelism over the sequence", last paragraph).
- *   q, k, v, dout   [B, N, H, d] bf16, the forward's inputs and the upstream gradient
+ *   q, dout         [B, N, H, d] bf16, the forward's query and the upstream gradient
+ *   k, v            [B, N, Hkv, d] bf16, the forward's keys and values
  *   o, lse          the forward's outputs for the same inputs (fa_fwd)
- *   dq, dk, dv      fp32 [B, N, H, d] (written). dq is cleared by the call and then
- *                   accumulated with device atomics; dk, dv are written once per
- *                   key block.
+ *   dq              fp32 [B, N, H, d] (written): cleared by the call, then accumulated
+ *                   with device atomics.
+ *   dk, dv          fp32 [B, N, Hkv, d] (written). With Hkv = H each element is written
+ *                   once per key block; with Hkv < H a shared head receives the sum of
+ *                   its group's gradients (cleared by the call, then added with device
+ *                   atomics).
  *   workspace       >= fa_bwd_workspace_bytes(B, H, N) bytes of device memory.
  * Probabilities are recomputed from Q, K and the saved LSE as exp(s - LSE); the
  * gradient is dV = P^T dO, dS = P * (dO V^T - D), dQ = scale dS K, dK = scale dS^T Q.
- * Only FA_DTYPE_BF16 is accepted. The order of the dq atomic additions varies
- * from run to run, so dq is reproducible to rounding, not bit for bit.
+ * Only FA_DTYPE_BF16 is accepted. The order of the atomic additions varies from
+ * run to run, so dq (and dk, dv when grouped) are reproducible to rounding, not
+ * bit for bit.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
            const void* dout, float* dq, float* dk, float* dv,
-           int B, int H, int N, int d, float scale, int causal, int dtype,
+           int B, int H, int Hkv, int N, int d, float scale, int causal, int dtype,
            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace fa_fwd_fp8 needs: the e4m3 codes of Q, K and V (one byte per

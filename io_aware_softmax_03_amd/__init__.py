@@ -10,13 +10,13 @@ memory and streams. Tensors must be contiguous device tensors:
                                                  q [B, Nq, H, d], k,v [B, Nk, Hkv, d]
     fwd_fp8(q, k, v, signs=None, scale=None, causal=False) -> (o, lse)   FP8 e4m3 compute
     fwd_varlen(q, k, v, cu_seqlens, max_seqlen, ...) -> (o, lse) q [T, H, d], k,v [T, Hkv, d]
-    bwd(q, k, v, o, lse, do, scale=None, causal=False) -> (dq, dk, dv)   fp32 grads
+    bwd(q, k, v, o, lse, do, scale=None, causal=False) -> (dq, dk, dv)   fp32 grads (dk, dv: Hkv heads)
     decode(q, k_cache, v_cache, scale=None, num_splits=64) -> (o, lse)   q [B, H, d]
     decode_paged(q, k_pages, v_pages, block_table, seqlens, ...) -> (o, lse)
 
 ``scale`` defaults to 1/sqrt(d). K and V may have fewer heads than Q (Hkv dividing H,
 grouped-query attention: query head h reads key-value head h // (H // Hkv)); the number
-is taken from their shapes. The backward is multi-head only.
+is taken from their shapes (the backward returns dK, dV with Hkv heads).
 """
 from __future__ import annotations
 
@@ -171,32 +171,37 @@ def fwd_varlen(q, k, v, cu_seqlens, max_seqlen, scale=None, causal=False):
 
 
 def bwd(q, k, v, o, lse, do, scale=None, causal=False, out=None, workspace=None):
-    """Backward from the forward's O and LSE. Returns fp32 dq, dk, dv [B, N, H, d].
-    ``out=(dq, dk, dv)`` and ``workspace`` may be preallocated."""
+    """Backward from the forward's O and LSE. Returns fp32 dq [B, N, H, d] and dk, dv
+    [B, N, Hkv, d]. ``out=(dq, dk, dv)`` and ``workspace`` may be preallocated."""
     torch = _torch()
     _require((q, k, v, o, lse, do), ("q", "k", "v", "o", "lse", "do"))
     B, N, H, d = q.shape
-    for t, n in ((k, "k"), (v, "v"), (o, "o"), (do, "do")):
+    for t, n in ((o, "o"), (do, "do")):
         if t.shape != q.shape or t.dtype != q.dtype:
             raise ValueError(f"{n} must match q in shape and dtype")
+    if k.dim() != 4 or k.shape[:2] != q.shape[:2] or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError("k, v must be [B, N, Hkv, d] matching q")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k, v must match q in dtype")
+    Hkv = k.shape[2]
     if lse.shape != (B, H, N) or lse.dtype != torch.float32:
         raise ValueError("lse must be fp32 [B, H, N]")
     if out is None:
         dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-        dk = torch.empty_like(dq)
-        dv = torch.empty_like(dq)
+        dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+        dv = torch.empty_like(dk)
     else:
         dq, dk, dv = out
         _require((dq, dk, dv), ("dq", "dk", "dv"))
-        for t in (dq, dk, dv):
-            if t.shape != q.shape or t.dtype != torch.float32:
-                raise ValueError("out gradients must be fp32 and shaped like q")
+        if dq.shape != q.shape or dk.shape != k.shape or dv.shape != k.shape or any(
+                t.dtype != torch.float32 for t in (dq, dk, dv)):
+            raise ValueError("out gradients must be fp32, dq shaped like q and dk, dv like k")
     nbytes = lib().fa_bwd_workspace_bytes(B, H, N)
     ws = workspace
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     st = lib().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
-                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, _scale(scale, d),
+                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, d, _scale(scale, d),
                       int(bool(causal)), _dtype_code(q), ws.data_ptr(), ws.numel(), _stream(q.device))
     check(st, "fa_bwd")
     return dq, dk, dv

@@ -24,7 +24,7 @@ SIGNATURES = {
     "fa_fwd_fp8_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "fa_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
     "fa_bwd_workspace_bytes": (_Z, [_I, _I, _I]),
-    "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
+    "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
     "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
     "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),

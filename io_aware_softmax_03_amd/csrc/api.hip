@@ -172,9 +172,9 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N) {
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-           float* dq, float* dk, float* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
-           void* workspace, size_t workspace_bytes, void* stream) {
-  if (B < 0 || N < 0 || H <= 0) return FA_ERR_SHAPE;
+           float* dq, float* dk, float* dv, int B, int H, int Hkv, int N, int d, float scale, int causal,
+           int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || N < 0 || N > kMaxSeq || !heads_ok(H, Hkv)) return FA_ERR_SHAPE;
   if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
   if (dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
   if (!scale_ok(scale) || (causal != 0 && causal != 1)) return FA_ERR_ARG;
@@ -185,7 +185,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, workspace};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FA_ERR_ARG;
-  fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, (float*)workspace, B, H, N, d, scale, causal != 0};
+  fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, (float*)workspace, B, H, Hkv, N, d, scale, causal != 0};
   return from_hip(fa::launch_bwd_bf16(a, (hipStream_t)stream));
 }
 

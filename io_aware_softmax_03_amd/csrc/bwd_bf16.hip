@@ -36,8 +36,11 @@ struct PreArgs {
   const float* lse;
   float* delta;  // D, then LSE * log2(e)
   float* dq;
+  float* dk;       // zeroed here when grouped (the main kernel then adds into it)
+  float* dv;
   int heads, seqlen;
-  long long rows;  // B * N * H
+  long long rows;     // B * N * H
+  long long rows_kv;  // B * N * Hkv rows of dK, dV to zero, or 0
 };
 
 template <int D>
@@ -59,6 +62,12 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(PreArgs p) {
     f32x4 z = {0.f, 0.f, 0.f, 0.f};
     *(f32x4*)(p.dq + off) = z;
     *(f32x4*)(p.dq + off + 4) = z;
+    if (row < p.rows_kv) {
+      *(f32x4*)(p.dk + off) = z;
+      *(f32x4*)(p.dk + off + 4) = z;
+      *(f32x4*)(p.dv + off) = z;
+      *(f32x4*)(p.dv + off + 4) = z;
+    }
   }
   // sum over the CH lanes of the row (CH divides 64, rows are lane-aligned)
 #pragma unroll
@@ -84,7 +93,7 @@ struct MainArgs {
   float* dq;
   float* dk;
   float* dv;
-  int heads, seqlen, nkb;
+  int heads, kv_heads, group, seqlen, nkb;  // query head h reads key-value head h / group
   int grid;         // workgroups launched
   long long rows;   // B * H * N: offset of the base-2 LSE in the workspace
   float scale, scale_log2;
@@ -153,8 +162,10 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
   }
   const int h = bh % p.heads, b = bh / p.heads;
   const int N = p.seqlen;
-  const size_t rs = (size_t)p.heads * D;
+  const size_t rs = (size_t)p.heads * D;        // Q, dO, dQ row stride
   const size_t base = ((size_t)b * N * p.heads + h) * D;
+  const size_t rsk = (size_t)p.kv_heads * D;    // K, V, dK, dV row stride
+  const size_t base_kv = ((size_t)b * N * p.kv_heads + h / p.group) * D;
   const float* dlt_g = p.delta + ((size_t)b * p.heads + h) * N;
   const float* lse_g = p.delta + (size_t)p.rows + ((size_t)b * p.heads + h) * N;  // base-2 LSE
 
@@ -170,8 +181,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
   for (int kk = 0; kk < KK; ++kk) {
     u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
     if (myk < N) {
-      xk = *(const u32x4*)(p.k + base + (size_t)myk * rs + 16 * kk + 8 * hh);
-      xv = *(const u32x4*)(p.v + base + (size_t)myk * rs + 16 * kk + 8 * hh);
+      xk = *(const u32x4*)(p.k + base_kv + (size_t)myk * rsk + 16 * kk + 8 * hh);
+      xv = *(const u32x4*)(p.v + base_kv + (size_t)myk * rsk + 16 * kk + 8 * hh);
     }
     kf[kk] = __builtin_bit_cast(bf16x8, xk);
     vf[kk] = __builtin_bit_cast(bf16x8, xv);
@@ -181,7 +192,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
     const int row = ci / CH, c = ci % CH;
     const int key = kb0 + row;
     u32x4 x = {0u, 0u, 0u, 0u};
-    if (key < N) x = *(const u32x4*)(p.k + base + (size_t)key * rs + c * 8);
+    if (key < N) x = *(const u32x4*)(p.k + base_kv + (size_t)key * rsk + c * 8);
     *(u32x4*)(s_k + row * D + ((c ^ swz_tr<D>(row)) << 3)) = x;
   }
 
@@ -404,16 +415,24 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
     dq_atomics(qstart + (nsteps - 1) * kBQ);
   }
 
-  // dK = scale * dS^T Q, dV = P^T dO; lane holds [key 8i + 4hh + j][dim db*32 + r]
+  // dK = scale * dS^T Q, dV = P^T dO; lane holds [key 8i + 4hh + j][dim db*32 + r]. A key-value
+  // head shared by a group of query heads sums the group's contributions (added into the
+  // zeroed dK, dV); otherwise each element is written once.
+  const bool grouped = p.group > 1;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = kw + 8 * (i >> 2) + 4 * hh + (i & 3);
       if (key < N) {
-        const size_t off = base + (size_t)key * rs + db * 32 + r;
-        p.dk[off] = dk_acc[db][i] * p.scale;
-        p.dv[off] = dv_acc[db][i];
+        const size_t off = base_kv + (size_t)key * rsk + db * 32 + r;
+        if (grouped) {
+          atomicAdd(p.dk + off, dk_acc[db][i] * p.scale);
+          atomicAdd(p.dv + off, dv_acc[db][i]);
+        } else {
+          p.dk[off] = dk_acc[db][i] * p.scale;
+          p.dv[off] = dv_acc[db][i];
+        }
       }
     }
 }
@@ -432,9 +451,12 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
   pre.lse = a.lse;
   pre.delta = a.delta;
   pre.dq = a.dq;
+  pre.dk = a.dk;
+  pre.dv = a.dv;
   pre.heads = a.heads;
   pre.seqlen = a.seqlen;
   pre.rows = (long long)a.batch * a.seqlen * a.heads;
+  pre.rows_kv = a.kv_heads < a.heads ? (long long)a.batch * a.seqlen * a.kv_heads : 0;
   const long long threads = pre.rows * (D / 8);
   const long long pblocks = (threads + 255) / 256;
   if (pblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
@@ -453,6 +475,8 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
   m.dk = a.dk;
   m.dv = a.dv;
   m.heads = a.heads;
+  m.kv_heads = a.kv_heads;
+  m.group = a.heads / a.kv_heads;
   m.seqlen = a.seqlen;
   m.nkb = (a.seqlen + kBK - 1) / kBK;
   m.scale = a.scale;

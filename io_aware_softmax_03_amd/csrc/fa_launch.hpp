@@ -44,7 +44,7 @@ struct BwdArgs {
   float* dk;
   float* dv;
   float* delta;  // workspace: D [B, H, N], then LSE * log2(e) [B, H, N]
-  int batch, heads, seqlen, head_dim;
+  int batch, heads, kv_heads, seqlen, head_dim;  // K, V, dK, dV have kv_heads heads
   float scale;
   bool causal;
 };

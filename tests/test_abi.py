@@ -129,7 +129,7 @@ def test_varlen_empty_is_noop():
 
 
 def bwd(**kw):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, H=2, N=64,
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, H=2, Hkv=2, N=64,
              d=128, scale=0.1, causal=1, dtype=_clib.FA_DTYPE_BF16, ws=FAKE, ws_bytes=1 << 20, stream=None)
     a.update(kw)
     return _clib.lib().fa_bwd(*a.values())
@@ -140,6 +140,7 @@ def bwd(**kw):
     (dict(ws_bytes=2 * 64 * 2 * 4 - 1), _clib.FA_ERR_WORKSPACE), (dict(dq=None), _clib.FA_ERR_NULL),
     (dict(d=80), _clib.FA_ERR_HEADDIM), (dict(scale=float("inf")), _clib.FA_ERR_ARG),
     (dict(dk=FAKE + 4), _clib.FA_ERR_ARG), (dict(H=-2), _clib.FA_ERR_SHAPE),
+    (dict(Hkv=3), _clib.FA_ERR_SHAPE), (dict(Hkv=0), _clib.FA_ERR_SHAPE), (dict(N=(1 << 30) + 1), _clib.FA_ERR_SHAPE),
 ])
 def test_bwd_rejects(kw, code):
     assert bwd(**kw) == code

@@ -159,3 +159,43 @@ def test_decode_gqa_full_size_sampled_heads():
     assert np.isfinite(o).all() and np.isfinite(lse).all()
     del kc, vc
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------------------ backward
+
+TOL_GRAD = 2e-2
+
+
+@pytest.mark.parametrize("B,N,H,Hkv,d,causal", [
+    (1, 256, 4, 2, 128, True),
+    (2, 300, 6, 3, 64, False),
+    (1, 200, 8, 1, 128, True),     # one key-value head for all eight query heads
+    (1, 513, 4, 2, 64, True),
+])
+def test_bwd_gqa(B, N, H, Hkv, d, causal):
+    q, k, v = gen(28, B, N, H, Hkv, d, "bf16")
+    g = synth.bnhd_tensor(28, synth.TENSOR_DO, B, N, H, d)
+    qd, kd, vd, gd = (dev_bf16(x) for x in (q, k, v, g))
+    o, lse = fa().fwd(qd, kd, vd, causal=causal)
+    dq, dk, dv = fa().bwd(qd, kd, vd, o, lse, gd, causal=causal)
+    ref = oracle.attn_bwd(bits_to_f64(q), bits_to_f64(k), bits_to_f64(v), bits_to_f64(g), 1 / math.sqrt(d), causal)
+    for got, want in zip((dq, dk, dv), ref):
+        assert got.shape == want.shape
+        assert max_abs(host(got), want) <= TOL_GRAD
+
+
+def test_bwd_gqa_equals_multi_head_on_repeated_heads_summed():
+    """dK, dV of a shared head equal the multi-head gradients of its repeated copies, summed
+    over the group (to the order of the fp32 additions); dQ is the same."""
+    torch = pytest.importorskip("torch")
+    B, N, H, Hkv, d = 1, 600, 8, 2, 128
+    q, k, v = (dev_bf16(x) for x in gen(29, B, N, H, Hkv, d, "bf16"))
+    g = dev_bf16(synth.bnhd_tensor(29, synth.TENSOR_DO, B, N, H, d))
+    grp = H // Hkv
+    kr, vr = k.repeat_interleave(grp, dim=2).contiguous(), v.repeat_interleave(grp, dim=2).contiguous()
+    o, lse = fa().fwd(q, k, v, causal=True)
+    dq, dk, dv = fa().bwd(q, k, v, o, lse, g, causal=True)
+    dq2, dk2, dv2 = fa().bwd(q, kr, vr, o, lse, g, causal=True)
+    assert max_abs(host(dq), host(dq2)) <= 1e-5
+    assert max_abs(host(dk), host(dk2.view(B, N, Hkv, grp, d).sum(dim=3))) <= 1e-4
+    assert max_abs(host(dv), host(dv2.view(B, N, Hkv, grp, d).sum(dim=3))) <= 1e-4
