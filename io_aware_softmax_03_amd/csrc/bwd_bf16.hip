@@ -6,7 +6,8 @@
 // backward is parallel over key blocks, dK_j and dV_j belong to one block, dQ_i is
 // accumulated with atomic additions in device memory).
 //
-// Kernel 1 (preprocess): D_i = sum_c dO_ic O_ic per row, LSE_i * log2(e), and dQ <- 0.
+// Kernel 1 (preprocess): D_i = sum_c dO_ic O_ic per row, LSE_i * log2(e), dQ <- 0 (and
+// dK, dV <- 0 when key-value heads are shared by groups of query heads).
 // Kernel 2 (main): one workgroup per (128-key block, batch*head); each of its 4 waves owns
 // 32 keys and keeps K, V (as MFMA operands) and dK, dV (fp32 accumulators) in registers.
 // It walks 32-query blocks (causal: only those that can see a key of the block); the Q and
@@ -18,7 +19,9 @@
 //   dS^T goes to LDS (double buffered); in the next step each wave forms 32 of the head dims
 //   of dQ_i = dS K over all 128 keys of the block, with its MFMAs running beside the
 //   exponentials of that step, and adds them into dQ with one fp32 atomic per element.
-// One workgroup barrier per query block.
+// One workgroup barrier per query block. Grouped-query attention: the workgroup of query
+// head h reads K, V of key-value head h / (H / Hkv) and adds its dK, dV into the shared
+// head's gradients with fp32 atomics; with Hkv = H they are stored once.
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 

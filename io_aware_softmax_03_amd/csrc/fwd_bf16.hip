@@ -17,13 +17,18 @@
 //     maximum exceeds it by more than kRescaleThreshold (exact for any shared pivot,
 //     "And on Blackwell"), so most blocks skip the accumulator rescale;
 //   * key blocks entirely above the causal diagonal are never loaded, and a wave stops at the
-//     last key block its rows can see.
-// gfx950 specifics: one wave per SIMD (512 registers: the output accumulators sit in AGPRs);
-// K and V tiles go from global memory straight into LDS (global_load_lds_dwordx4, lane i ->
-// bytes 16i of a wave's 1 KB slice), each lane picking the source chunk that lands it at its
-// swizzled position. Within a wave the loop is a three-stage software pipeline: while the
-// MFMAs of the next block's scores and of the previous block's P V run, the VALU turns this
-// block's scores into probabilities.
+//     last key block its rows can see. The mask is general: query i sees key j when
+//     i + lo_off <= j <= i + hi_off (bottom-right causal for Nq != Nk, sliding windows;
+//     "Using it, the real way"); a query block loads only the key blocks between its first
+//     row's lowest and last row's highest visible key, and with a window each wave starts
+//     at its own first block;
+//   * grouped-query attention: query head h reads key-value head h / (H / Hkv).
+// gfx950 specifics: one wave per SIMD (512 registers: output accumulators and score tiles in
+// VGPRs, the Q operands in AGPRs); K and V tiles go from global memory straight into LDS
+// (buffer loads with an LDS destination, lane i -> bytes 16i of a wave's 1 KB slice), each
+// lane picking the source chunk that lands it at its swizzled position. Within a wave the
+// loop is a three-stage software pipeline: while the MFMAs of the next block's scores and
+// of the previous block's P V run, the VALU turns this block's scores into probabilities.
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 

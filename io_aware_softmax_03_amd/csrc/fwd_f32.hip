@@ -5,7 +5,8 @@
 // precision matrix cores, so results stay within fp32 rounding of the exact value.
 // Each query row is owned by 8 consecutive lanes (D/8 head dims each), so a dot product is
 // a short per-lane FMA chain plus a three-step butterfly; K and V blocks of 32 keys are
-// staged in LDS.
+// staged in LDS. It takes the same general mask as the bf16 kernel (query i sees key j
+// when i + lo_off <= j <= i + hi_off) and grouped key-value heads.
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
