@@ -13,9 +13,12 @@
 //     max / row sum are in-lane plus one swap between wave halves;
 //   * O^T += V^T P^T on MFMA, with P^T taken straight from the score registers and V^T read
 //     from the row-major V tile with the LDS transpose read;
-//   * online softmax in base 2 on scaled scores; the pivot is only moved when a block's
-//     maximum exceeds it by more than kRescaleThreshold (exact for any shared pivot,
-//     "And on Blackwell"), so most blocks skip the accumulator rescale;
+//   * online softmax in base 2 on scaled scores against a pivot that moves only when a
+//     block's values exceed it by more than kRescaleThreshold (exact for any shared pivot,
+//     "And on Blackwell"): a wave's first block sets it from its row maximum; after that no
+//     row maximum is taken, P is formed against the current pivot and a lane sum above
+//     2^kRescaleThreshold (rare) sends the block through a path that forms its scores again,
+//     moves the pivot to their maximum and rescales O and the sums;
 //   * key blocks entirely above the causal diagonal are never loaded, and a wave stops at the
 //     last key block its rows can see. The mask is general: query i sees key j when
 //     i + lo_off <= j <= i + hi_off (bottom-right causal for Nq != Nk, sliding windows;
@@ -40,6 +43,7 @@ constexpr int kNW = 4;   // waves per workgroup
 constexpr int kQW = 64;  // query rows per wave
 constexpr int kBR = kNW * kQW;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: P stays <= 256
+constexpr float kPMax = 256.0f;            // 2^kRescaleThreshold
 
 struct FwdKernelArgs {
   const uint16_t* q;
@@ -328,8 +332,22 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
       ma = max3(ma, s[14], s[15]);
       return pair_max(fmaxf(ma, mb)) * c2;
     };
-    // Move a group's pivot when the block maximum exceeds it by more than the threshold
-    // (rare), rescaling O, both sums and the P block not yet multiplied into O.
+    // O and both sums of group g times alpha (after its pivot moved up by -log2(alpha))
+    auto rescale = [&](int g, float alpha) {
+      l_part[g] *= alpha;
+      lr_part[g] *= alpha;
+      lsum[g] *= __int_as_float(__builtin_amdgcn_ds_bpermute(4 * lane_q16, __float_as_int(alpha)));
+      // one 16-register block at a time, so this rare path does not raise the kernel's
+      // register count
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[g][db][i] *= alpha;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // Before a wave's first block: move a group's pivot when the block maximum exceeds it by
+    // more than the threshold, rescaling the P block not yet multiplied into O as well.
     auto repivot = [&](const float (&mt)[2], bf16x8 (&pend)[2][KS]) {
       const bool up = mt[0] > m_ref[0] + kRescaleThreshold || mt[1] > m_ref[1] + kRescaleThreshold;
       if (wave_any(up)) {
@@ -337,20 +355,10 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
         for (int g = 0; g < 2; ++g) {
           const float m_new = fmaxf(m_ref[g], mt[g]);
           const float alpha = exp2_fast(m_ref[g] - m_new);
-          l_part[g] *= alpha;
-          lr_part[g] *= alpha;
-          lsum[g] *= __int_as_float(__builtin_amdgcn_ds_bpermute(4 * lane_q16, __float_as_int(alpha)));
-          // one 16-register block at a time (the accumulators are in AGPRs: each value goes
-          // through a VGPR), so this rare path does not raise the kernel's register count
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[g][db][i] *= alpha;
-            __builtin_amdgcn_sched_barrier(0);
-          }
+          m_ref[g] = m_new;
+          rescale(g, alpha);
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) pend[g][ks] = scale_bf16x8(pend[g][ks], alpha);
-          m_ref[g] = m_new;
         }
       }
     };
@@ -374,6 +382,51 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
           s[0] = mfma32(a, qf[0][kk], s[0]);
           s[1] = mfma32(a, qf[1][kk], s[1]);
         }
+      }
+    };
+    // A P block with a value above kPMax (a lane's sum of its 16 values says so, inf
+    // included): the block's scores exceed the running pivot by more than the threshold,
+    // which is rare. S is formed again from K in global memory (the block's LDS copy has been
+    // overwritten by then), the pivot moves to the block's maximum, and the block's P (fp32
+    // sums into bs, bf16 operands into pb) is redone with it; the factor O and the running sums
+    // must be multiplied by goes to alpha.
+    auto rescue = [&](int k0, bf16x8 (&pb)[2][KS], float (&bs)[2], float (&alpha)[2]) {
+      const uint16_t* krow = kg + (size_t)min(k0 + r, Lk - 1) * rsk + 8 * hh;
+      // one query group at a time and one K operand at a time (scheduling barriers keep the
+      // loads from being hoisted), so this path needs few registers beyond the step's own
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        f32x16 sg[1];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(krow + 16 * kk));
+          sg[0] = mfma32(a, qf[g][kk], kk == 0 ? f32x16{} : sg[0]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (edge(k0)) {
+          const int row = qw + 32 * g + r;
+          const int lim = CAUSAL ? min(row + p.hi_off, Lk - 1) : Lk - 1;
+          const int low = row + p.lo_off;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kl = k0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+            sg[0][i] = (kl > lim || (WINDOW && kl < low)) ? -INFINITY : sg[0][i];
+          }
+        }
+        const float m_new = fmaxf(m_ref[g], rowmax(sg[0]));
+        alpha[g] = exp2_fast(m_ref[g] - m_new);
+        m_ref[g] = m_new;
+        bs[g] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sg[0][i] = exp2_fast(__builtin_fmaf(sg[0][i], c2, -m_ref[g]));
+          bs[g] += sg[0][i];
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          pb[g][ks] = pack_bf16x8(sg[0][8 * ks], sg[0][8 * ks + 1], sg[0][8 * ks + 2], sg[0][8 * ks + 3],
+                                  sg[0][8 * ks + 4], sg[0][8 * ks + 5], sg[0][8 * ks + 6], sg[0][8 * ks + 7]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
     // V^T operand of k-step ks, output block db, from V buffer BUF
@@ -404,10 +457,10 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
     // Values a pipeline part produces are pinned in VGPRs at its end, so that neither the IR
     // optimisers (which would sink them past the part, next to their first use) nor the
     // register allocator (AGPRs) move them out of the part they are scheduled in.
-    auto pin = [&](bf16x8 (&pb)[KS], float& a, float (&b)[2]) {
+    auto pin = [&](bf16x8 (&pb)[KS], float& a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(pb[ks]));
-      asm volatile("" : "+v"(a), "+v"(b[0]), "+v"(b[1]));
+      asm volatile("" : "+v"(a));
     };
 
     using B0 = std::integral_constant<int, 0>;
@@ -451,8 +504,9 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
     // The step is laid out by hand as NSLOT slots, one MFMA each (the score MFMAs first, then
     // those of P V), fenced by scheduling barriers. Each slot also carries a fixed share of
     // the VALU work on P(j) (scale-and-shift FMA, exponential, fp32 sum, bf16 packing), the
-    // rounded sums of P(j-1), the row maximum of S(j+1) once its MFMAs are done, and LDS
-    // reads a few slots ahead of the MFMA that consumes them.
+    // rounded sums of P(j-1), and LDS reads a few slots ahead of the MFMA that consumes them.
+    // P(j) is formed with the current pivot; no row maximum is taken. The lane sums of P(j)
+    // bound its values: when one exceeds kPMax (rare) the block is redone with a new pivot.
     constexpr int NQK = 2 * KK;               // score MFMAs (both query groups)
     constexpr int NSLOT = NQK + 2 * KS * DB;  // + P V MFMAs
     constexpr int VPS = 32 / NSLOT;           // probabilities per slot (1 for D=128, 2 for D=64)
@@ -470,11 +524,6 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
       const int t = NQK + 2 * DB * ks + 2 * db - 6 + hf;
       return t < -1 ? -1 : t;
     };
-    // row-maximum op k (0..9) of query group g
-    auto rmax_slot = [](int g, int k) {
-      const int base = NQK + 2 + g * ((NSLOT - NQK - 2) / 2);
-      return base + k / 2 < NSLOT ? base + k / 2 : NSLOT;
-    };
 
     auto step = [&](auto phase, int j) {
       constexpr int PH = decltype(phase)::value;
@@ -488,9 +537,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
       const float mneg[2] = {-m_ref[0], -m_ref[1]};
       bf16x8 ka[3];
       i16x4 vlo[KS][DB], vhi[KS][DB];
-      float acc[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-      bf16x2 pr[16];  // P(j) pairs: pair q holds values 2q, 2q+1 (value v = 16g + i is c[g][i])
-      float ma[2], mb[2], mt[2];
+      float acc[2][4];  // four partial fp32 sums of P(j) per query group
+      bf16x2 pr[16];    // P(j) pairs: pair q holds values 2q, 2q+1 (value v = 16g + i is c[g][i])
 
       auto slot = [&](auto tc) {
         constexpr int t = decltype(tc)::value;
@@ -522,7 +570,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
           const int g = v / 16, i = v % 16;
           if ((fma_slot(v) < -1 ? -1 : fma_slot(v)) == t) c[g][i] = __builtin_fmaf(c[g][i], c2, mneg[g]);
           if (exp_slot(v) == t) c[g][i] = exp2_fast(c[g][i]);
-          if (add_slot(v) == t) acc[g][i % 4] += c[g][i];
+          if (add_slot(v) == t) acc[g][i % 4] = i < 4 ? c[g][i] : acc[g][i % 4] + c[g][i];
         }
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
@@ -536,22 +584,6 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
 #pragma unroll
         for (int k = 0; k < 2 * KS; ++k)
           if (lsum_slot(k) == t) lsum[k / KS] = mfma16(sel, pp[k / KS][k % KS], lsum[k / KS]);
-        // row maximum of S(j+1): ten ops per query group
-#pragma unroll
-        for (int g = 0; g < 2; ++g)
-#pragma unroll
-          for (int k = 0; k < 10; ++k) {
-            if (rmax_slot(g, k) != t) continue;
-            if (k == 0) ma[g] = max3(n[g][0], n[g][1], n[g][2]);
-            if (k == 1) mb[g] = max3(n[g][3], n[g][4], n[g][5]);
-            if (k >= 2 && k <= 6) {
-              if (k % 2 == 0) ma[g] = max3(ma[g], n[g][2 * k + 2], n[g][2 * k + 3]);
-              else mb[g] = max3(mb[g], n[g][2 * k + 2], n[g][2 * k + 3]);
-            }
-            if (k == 7) ma[g] = fmaxf(ma[g], mb[g]);
-            if (k == 8) ma[g] = pair_max(ma[g]);
-            if (k == 9) mt[g] = ma[g] * c2;
-          }
         __builtin_amdgcn_sched_barrier(0);
       };
 
@@ -562,9 +594,10 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
       issue(VT(), std::integral_constant<int, PH>(), j);
       __builtin_amdgcn_sched_barrier(0);
       static_for<0, NSLOT + 1>(slot);
-      // tail: fold the partial sums, assemble the bf16 operands of P(j)
+      // tail: this lane's sums of P(j), the bf16 operands of P(j)
+      float bs[2];
 #pragma unroll
-      for (int g = 0; g < 2; ++g) l_part[g] += (acc[g][0] + acc[g][1]) + (acc[g][2] + acc[g][3]);
+      for (int g = 0; g < 2; ++g) bs[g] = (acc[g][0] + acc[g][1]) + (acc[g][2] + acc[g][3]);
 #pragma unroll
       for (int g = 0; g < 2; ++g)
 #pragma unroll
@@ -574,19 +607,23 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
                                               __builtin_shufflevector(pr[q + 2], pr[q + 3], 0, 1, 2, 3),
                                               0, 1, 2, 3, 4, 5, 6, 7);
         }
-      pin(pc[0], l_part[0], lr_part);
+      pin(pc[0], bs[0]);
       asm volatile("" : "+v"(lsum[0]), "+v"(lsum[1]));
-      pin(pc[1], l_part[1], mt);
+      pin(pc[1], bs[1]);
       __builtin_amdgcn_sched_barrier(0);
-      if (j + 1 < wtiles) {
-        // a diagonal or ragged block is masked, and its maximum taken, only now
-        if (edge(kb0 + (j + 1) * kBC)) {
-          mask(n, kb0 + (j + 1) * kBC);
-          mt[0] = rowmax(n[0]);
-          mt[1] = rowmax(n[1]);
-        }
-        repivot(mt, pc);
+      // (the rescale of O sits in a branch of its own: inside the rescue branch it made the
+      // register allocator move output accumulators through AGPRs on every step)
+      const bool over = wave_any(bs[0] > kPMax || bs[1] > kPMax);
+      float alpha[2];
+      if (over) rescue(kb0 + j * kBC, pc, bs, alpha);
+      // a diagonal or ragged block is masked only now
+      if (j + 1 < wtiles && edge(kb0 + (j + 1) * kBC)) mask(n, kb0 + (j + 1) * kBC);
+      if (over) {
+        rescale(0, alpha[0]);
+        rescale(1, alpha[1]);
       }
+      l_part[0] += bs[0];
+      l_part[1] += bs[1];
       __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of K(j+2), V(j) have landed
       __syncthreads();
     };

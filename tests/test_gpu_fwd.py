@@ -84,6 +84,28 @@ def test_fwd_bf16_large_scores_rescale():
         assert max_abs(host(lse), lse_ref) <= TOL_LSE_BF16
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_bf16_score_spikes_past_overflow(causal):
+    """Keys whose scores jump far above every earlier score (by more than 128 in base-2
+    units, so exp2 of the score against the old running maximum overflows fp32): the block
+    holding each spike must be redone against a new maximum. Values are exact in bf16."""
+    B, N, H, d = 1, 900, 2, 128
+    rng = np.random.default_rng(11)
+    q = np.full((B, N, H, d), 2.0)
+    k = np.round(rng.standard_normal((B, N, H, d)) * 8) / 8
+    v = np.round(rng.standard_normal((B, N, H, d)) * 8) / 8
+    k[:, 300] = 4.0     # score 2*4*128/sqrt(128), about 90.5 (130 base-2 units above the rest)
+    k[:, 650] = 8.0     # about 181
+    k[:, 651] = -8.0    # a large negative score right after
+    to = lambda x: dev_bf16(synth.bf16_bits_from_f32(x.astype(np.float32)))  # noqa: E731
+    o, lse = fa().fwd(to(q), to(k), to(v), causal=causal)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, 1 / math.sqrt(d), causal)
+    o, lse = host(o), host(lse)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    assert max_abs(o, o_ref) <= TOL_O_BF16
+    assert max_abs(lse, lse_ref) <= TOL_LSE_BF16
+
+
 def test_fwd_bf16_full_size_sampled_rows():
     """Causal B=2, H=16, N=8192, d=128 in the launch configuration the bench times; sampled
     rows of sampled heads are checked against the oracle row by row."""
