@@ -14,10 +14,10 @@
 //   * O^T += V^T P^T on MFMA, with P^T taken straight from the score registers and V^T read
 //     from the row-major V tile with the LDS transpose read;
 //   * online softmax in base 2 on scaled scores against a pivot that moves only when a
-//     block's values exceed it by more than kRescaleThreshold (exact for any shared pivot,
+//     block's values exceed it by more than a threshold (exact for any shared pivot,
 //     "And on Blackwell"): a wave's first block sets it from its row maximum; after that no
 //     row maximum is taken, P is formed against the current pivot and a lane sum above
-//     2^kRescaleThreshold (rare) sends the block through a path that forms its scores again,
+//     kPMax = 2^16 (rare) sends the block through a path that forms its scores again,
 //     moves the pivot to their maximum and rescales O and the sums;
 //   * key blocks entirely above the causal diagonal are never loaded, and a wave stops at the
 //     last key block its rows can see. The mask is general: query i sees key j when
@@ -42,8 +42,13 @@ constexpr int kBC = 32;  // keys per streamed block
 constexpr int kNW = 4;   // waves per workgroup
 constexpr int kQW = 64;  // query rows per wave
 constexpr int kBR = kNW * kQW;
-constexpr float kRescaleThreshold = 8.0f;  // log2 units: P stays <= 256
-constexpr float kPMax = 256.0f;            // 2^kRescaleThreshold
+constexpr float kRescaleThreshold = 8.0f;  // log2 units, for a wave's first block: P <= 256
+// Bound on P after the first block. The result is exact for any pivot; the bound only keeps
+// the fp32 accumulators far from overflow (O <= 2^16 * keys * max|V|). A larger bound than
+// the first block's 2^8 matters: a pivot taken from a block with few visible keys (first
+// rows of a causal or windowed sequence) or on large-magnitude scores is often exceeded by 8,
+// and every such block would go through the rescue path.
+constexpr float kPMax = 65536.0f;
 
 struct FwdKernelArgs {
   const uint16_t* q;

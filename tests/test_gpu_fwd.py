@@ -84,19 +84,25 @@ def test_fwd_bf16_large_scores_rescale():
         assert max_abs(host(lse), lse_ref) <= TOL_LSE_BF16
 
 
+@pytest.mark.parametrize("spikes", [
+    (4.0, 8.0),     # scores about 90.5 and 181 (130 and 260 base-2 units above the rest):
+                    # exp2 against the old pivot overflows fp32
+    (0.5, 1.0),     # about 11.3 and 22.6: the first stays under the kernel's bound on P
+                    # (P in the thousands, no rescue), the second goes past it (no inf)
+])
 @pytest.mark.parametrize("causal", [False, True])
-def test_fwd_bf16_score_spikes_past_overflow(causal):
-    """Keys whose scores jump far above every earlier score (by more than 128 in base-2
-    units, so exp2 of the score against the old running maximum overflows fp32): the block
-    holding each spike must be redone against a new maximum. Values are exact in bf16."""
+def test_fwd_bf16_score_spikes_past_overflow(causal, spikes):
+    """Keys whose scores jump far above every earlier score: the block holding each spike
+    must be redone against a new maximum, or carried with large P where no accumulator can
+    overflow. Values are exact in bf16."""
     B, N, H, d = 1, 900, 2, 128
     rng = np.random.default_rng(11)
     q = np.full((B, N, H, d), 2.0)
     k = np.round(rng.standard_normal((B, N, H, d)) * 8) / 8
     v = np.round(rng.standard_normal((B, N, H, d)) * 8) / 8
-    k[:, 300] = 4.0     # score 2*4*128/sqrt(128), about 90.5 (130 base-2 units above the rest)
-    k[:, 650] = 8.0     # about 181
-    k[:, 651] = -8.0    # a large negative score right after
+    k[:, 300] = spikes[0]    # score 2*c*128/sqrt(128)
+    k[:, 650] = spikes[1]
+    k[:, 651] = -spikes[1]   # a large negative score right after
     to = lambda x: dev_bf16(synth.bf16_bits_from_f32(x.astype(np.float32)))  # noqa: E731
     o, lse = fa().fwd(to(q), to(k), to(v), causal=causal)
     o_ref, lse_ref = oracle.attn_fwd(q, k, v, 1 / math.sqrt(d), causal)
