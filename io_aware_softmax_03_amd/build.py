@@ -32,10 +32,13 @@ FLAGS = [
 # default the compiler then gives every MFMA the AGPR accumulator form, which would put the
 # score tiles in AGPRs and cost a copy to VGPRs for each softmax step. With the VGPR form the
 # output accumulators and scores sit in VGPRs and the Q operands in AGPRs.
-# The FP8 forward kernel needs the same form to stay out of scratch memory.
+# The FP8 forward kernel needs the same form to stay out of scratch memory. In the backward
+# kernel the AGPR form copied every score, dP and dQ tile between the register files each
+# step.
 FILE_FLAGS = {
     "fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "fwd_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -258,32 +258,45 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
 
   f32x16 dq_acc;  // dQ of the previous query block: lane holds [query 8i + 4hh + j][dim wid*QCOLS + r]
   // dQ_{i} of this wave's head dims = dS_i K over the 128 keys of the block (dS^T from LDS)
-  auto dq_mfma = [&](auto bufc, int q0) {
+  auto dq_mfma = [&](auto bufc) {
     const uint16_t* sds = s_ds[decltype(bufc)::value];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) dq_acc[i] = 0.f;
-    const int kmax = CAUSAL ? min(kBK, q0 + kBQ - kb0) : kBK;  // keys past the last query give dS = 0
+    // (all 128 keys, also on diagonal blocks: keys past the block's last query hold dS = 0,
+    // and a branch per k-step would keep these products from interleaving with the step's
+    // exponentials)
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
-      if (16 * ks < kmax) {
-        const int row_a = 16 * ks + 4 * hh + (gi >> 2);
-        const int row_b = row_a + 8;
-        const int qc = 16 * nh + 4 * (gi & 3);
-        const bf16x8 ads = join_tr(lds_read_tr(sds + ds_off(row_a, qc)), lds_read_tr(sds + ds_off(row_b, qc)));
-        dq_acc = mfma32(ads, kq[ks], dq_acc);
-      }
+      const int row_a = 16 * ks + 4 * hh + (gi >> 2);
+      const int row_b = row_a + 8;
+      const int qc = 16 * nh + 4 * (gi & 3);
+      const bf16x8 ads = join_tr(lds_read_tr(sds + ds_off(row_a, qc)), lds_read_tr(sds + ds_off(row_b, qc)));
+      dq_acc = mfma32(ads, kq[ks], ks == 0 ? f32x16{} : dq_acc);
     }
   };
   // Exactly kDqAtomics atomic instructions per call (rows past the end add 0 to the last
   // row), so the step's wait can leave them in flight: see step_sync.
+  // A whole query block goes through buffer atomics: the block's wave-uniform base in the
+  // buffer resource, the lane's offset in one VGPR, the row of accumulator element i in the
+  // scalar offset, so no address arithmetic runs per atomic. Only the ragged last block (or a
+  // block whose 32 rows span 4 GB or more) clamps rows one by one.
+  const unsigned rs4 = (unsigned)rs * 4u;                                // dQ row stride, bytes
+  const unsigned dq_lane = (unsigned)(4 * hh) * rs4 + 4u * (unsigned)r;   // lane's offset in a block
+  const bool dq_buf = (size_t)rs * 4u * kBQ <= 0xffffffffu;
   auto dq_atomics = [&](int q0) {
     if (QCOLS == 32 || r < 16) {
-      float* dqg = p.dq + base + wid * QCOLS + r;
+      if (dq_buf && q0 + kBQ <= N) {
+        const __amdgpu_buffer_rsrc_t rdq = make_rsrc(p.dq + base + (size_t)q0 * rs + wid * QCOLS, rs4 * kBQ);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int qi = q0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-        const float x = qi < N ? dq_acc[i] * p.scale : 0.f;
-        atomicAdd(dqg + (size_t)min(qi, N - 1) * rs, x);
+        for (int i = 0; i < 16; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(dq_acc[i] * p.scale, rdq, dq_lane,
+                                                          (int)((8 * (i >> 2) + (i & 3)) * rs4), 0);
+      } else {
+        float* dqg = p.dq + base + wid * QCOLS + r;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int qi = q0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+          const float x = qi < N ? dq_acc[i] * p.scale : 0.f;
+          atomicAdd(dqg + (size_t)min(qi, N - 1) * rs, x);
+        }
       }
     }
   };
@@ -322,13 +335,36 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
     const uint16_t* sd = B ? s_do1 : s_do0;
 
     f32x16 sc, dp;  // S and dP: lane = key r, acc[4i+j] = query 8i + 4hh + j
+    // the tile's base-2 LSE and D for this lane's queries, read now so they have landed by
+    // the time P and dS are formed
+    f32x4 l4[4], d4[4];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const int c = 2 * kk + hh;
-      const bf16x8 aq = __builtin_bit_cast(bf16x8, *(const u32x4*)(sq + r * D + ((c ^ swz_row<D>(r)) << 3)));
-      const bf16x8 ad = __builtin_bit_cast(bf16x8, *(const u32x4*)(sd + r * D + ((c ^ swz_row<D>(r)) << 3)));
-      sc = mfma32(aq, kf[kk], kk == 0 ? f32x16{} : sc);
-      dp = mfma32(ad, vf[kk], kk == 0 ? f32x16{} : dp);
+    for (int i4 = 0; i4 < 4; ++i4) {
+      l4[i4] = *(const f32x4*)((const float*)(sq + QT) + 8 * i4 + 4 * hh);
+      d4[i4] = *(const f32x4*)((const float*)(sq + QT + 2 * kBQ) + 8 * i4 + 4 * hh);
+    }
+    {
+      // Q and dO operands of k-step kk are read two k-steps ahead of their MFMAs
+      bf16x8 aq[KK], ad[KK];
+      auto rd = [&](int kk) {
+        const int c = 2 * kk + hh;
+        aq[kk] = __builtin_bit_cast(bf16x8, *(const u32x4*)(sq + r * D + ((c ^ swz_row<D>(r)) << 3)));
+        ad[kk] = __builtin_bit_cast(bf16x8, *(const u32x4*)(sd + r * D + ((c ^ swz_row<D>(r)) << 3)));
+      };
+      rd(0);
+      rd(1);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        if (kk + 2 < KK) rd(kk + 2);
+        sc = mfma32(aq[kk], kf[kk], kk == 0 ? f32x16{} : sc);
+        dp = mfma32(ad[kk], vf[kk], kk == 0 ? f32x16{} : dp);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 12, 2);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        if (kk + 2 < KK) __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 2);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     const bool edge = (CAUSAL && q0 < kw + 31) || (q0 + kBQ > N) || (kw + 32 > N);
@@ -339,18 +375,33 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
         if ((CAUSAL && myk > qi) || myk >= N) sc[i] = -INFINITY;
       }
     }
-    // P, dS of this tile beside the dQ MFMAs of the previous tile
-    dq_mfma(NB(), q0 - kBQ);
+    // P, dS of this tile beside the dQ MFMAs of the previous tile, laid out by hand in eight
+    // chunks fenced by scheduling barriers: chunk t issues dQ MFMA t (its dS^T operand was
+    // read two chunks earlier), the operand reads of k-step t + 2, and the VALU work of two
+    // of the sixteen P, dS values, which runs while the MFMA does.
     f32x16 pr, ds;
+    {
+      const uint16_t* sds = s_ds[B ^ 1];
+      bf16x8 ads[kBK / 16];
+      auto rdq = [&](int ks) {
+        const int row_a = 16 * ks + 4 * hh + (gi >> 2);
+        const int row_b = row_a + 8;
+        const int qc = 16 * nh + 4 * (gi & 3);
+        ads[ks] = join_tr(lds_read_tr(sds + ds_off(row_a, qc)), lds_read_tr(sds + ds_off(row_b, qc)));
+      };
+      rdq(0);
+      rdq(1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const f32x4 l4 = *(const f32x4*)((const float*)(sq + QT) + 8 * i4 + 4 * hh);
-      const f32x4 d4 = *(const f32x4*)((const float*)(sq + QT + 2 * kBQ) + 8 * i4 + 4 * hh);
+      for (int t = 0; t < kBK / 16; ++t) {
+        if (t + 2 < kBK / 16) rdq(t + 2);
+        dq_acc = mfma32(ads[t], kq[t], t == 0 ? f32x16{} : dq_acc);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 4 * i4 + j;
-        pr[i] = exp2_fast(__builtin_fmaf(sc[i], p.scale_log2, -l4[j]));
-        ds[i] = pr[i] * (dp[i] - d4[j]);
+        for (int i = 2 * t; i < 2 * t + 2; ++i) {
+          pr[i] = exp2_fast(__builtin_fmaf(sc[i], p.scale_log2, -l4[i >> 2][i & 3]));
+          ds[i] = pr[i] * (dp[i] - d4[i >> 2][i & 3]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     bf16x8 ap[2], as[2];
@@ -374,29 +425,38 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
       asm volatile("ds_write_b64 %0, %1" ::"v"(dst + 2u * ds_off(row, 16 + 4 * hh)), "v"(v2) : "memory");
       asm volatile("ds_write_b64 %0, %1" ::"v"(dst + 2u * ds_off(row, 24 + 4 * hh)), "v"(v3) : "memory");
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-#pragma unroll
-    for (int i = 0; i < 7; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
     __builtin_amdgcn_sched_barrier(0);
     if (st > 0) dq_atomics(q0 - kBQ);  // the dQ MFMAs have finished by now
-    // dV += P^T dO, dK += dS^T Q  (k-step ks: queries 16ks + 8(e/4) + 4hh + e%4)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int row_a = 16 * ks + 4 * hh + (gi >> 2);
-      const int row_b = row_a + 8;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
+    // dV += P^T dO, dK += dS^T Q  (k-step ks: queries 16ks + 8(e/4) + 4hh + e%4). Operand
+    // pair t = (ks, db) is read from LDS two pairs ahead of its MFMAs, so each read has two
+    // pairs of products to land behind.
+    {
+      constexpr int NP = 2 * DB;
+      bf16x8 bdo[NP], bq[NP];
+      auto rd = [&](int t) {
+        const int ks = t / DB, db = t % DB;
+        const int row_a = 16 * ks + 4 * hh + (gi >> 2);
+        const int row_b = row_a + 8;
         const int col = db * 32 + 16 * nh + 4 * (gi & 3);
         const int ca = (((col >> 3) ^ swz_row<D>(row_a)) << 3) + (col & 7);
         const int cb = (((col >> 3) ^ swz_row<D>(row_b)) << 3) + (col & 7);
-        const bf16x8 bdo = join_tr(lds_read_tr(sd + row_a * D + ca), lds_read_tr(sd + row_b * D + cb));
-        const bf16x8 bq = join_tr(lds_read_tr(sq + row_a * D + ca), lds_read_tr(sq + row_b * D + cb));
-        dv_acc[db] = mfma32(ap[ks], bdo, dv_acc[db]);
-        dk_acc[db] = mfma32(as[ks], bq, dk_acc[db]);
+        bdo[t] = join_tr(lds_read_tr(sd + row_a * D + ca), lds_read_tr(sd + row_b * D + cb));
+        bq[t] = join_tr(lds_read_tr(sq + row_a * D + ca), lds_read_tr(sq + row_b * D + cb));
+      };
+      rd(0);
+      rd(1);
+#pragma unroll
+      for (int t = 0; t < NP; ++t) {
+        if (t + 2 < NP) rd(t + 2);
+        const int ks = t / DB, db = t % DB;
+        dv_acc[db] = mfma32(ap[ks], bdo[t], dv_acc[db]);
+        dk_acc[db] = mfma32(as[ks], bq[t], dk_acc[db]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+#pragma unroll
+      for (int t = 0; t < NP; ++t) {
+        if (t + 2 < NP) __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -413,8 +473,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
   }
   // dQ of the last query block
   if (nsteps > 0) {
-    if ((nsteps - 1) & 1) dq_mfma(std::integral_constant<int, 1>(), qstart + (nsteps - 1) * kBQ);
-    else dq_mfma(std::integral_constant<int, 0>(), qstart + (nsteps - 1) * kBQ);
+    if ((nsteps - 1) & 1) dq_mfma(std::integral_constant<int, 1>());
+    else dq_mfma(std::integral_constant<int, 0>());
     dq_atomics(qstart + (nsteps - 1) * kBQ);
   }
 
