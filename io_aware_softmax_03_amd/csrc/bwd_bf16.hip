@@ -280,23 +280,22 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
         if ((CAUSAL && myk > qi) || myk >= N) sc[i] = -INFINITY;
       }
     }
+    // P, dS, then dV += P^T dO, dK += dS^T Q (k-step ks: queries 16ks + 8(e/4) + 4hh + e%4),
+    // laid out by hand in chunks fenced by scheduling barriers so that the VALU work of
+    // k-step 1 runs beside the MFMAs of k-step 0: chunk 0 reads the operands of k-step 0 and
+    // forms its P and dS; chunk db issues the two MFMAs of (k-step 0, block db), reads the
+    // operands of (k-step 1, block db) and forms 8 / DB values of k-step 1; then the MFMAs
+    // of k-step 1.
     f32x16 pr, ds;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    auto pds = [&](int i) {
       pr[i] = exp2_fast(__builtin_fmaf(sc[i], p.scale_log2, -l4[i >> 2][i & 3]));
       ds[i] = pr[i] * (dp[i] - d4[i >> 2][i & 3]);
-    }
-    bf16x8 ap[2], as[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    };
+    auto pack_ks = [&](int ks, bf16x8& a_p, bf16x8& a_s) {
       const int o8 = 8 * ks;
-      ap[ks] = pack_bf16x8(pr[o8], pr[o8 + 1], pr[o8 + 2], pr[o8 + 3], pr[o8 + 4], pr[o8 + 5], pr[o8 + 6], pr[o8 + 7]);
-      as[ks] = pack_bf16x8(ds[o8], ds[o8 + 1], ds[o8 + 2], ds[o8 + 3], ds[o8 + 4], ds[o8 + 5], ds[o8 + 6], ds[o8 + 7]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // dV += P^T dO, dK += dS^T Q  (k-step ks: queries 16ks + 8(e/4) + 4hh + e%4). Operand
-    // pair t = (ks, db) is read from LDS two pairs ahead of its MFMAs, so each read has two
-    // pairs of products to land behind.
+      a_p = pack_bf16x8(pr[o8], pr[o8 + 1], pr[o8 + 2], pr[o8 + 3], pr[o8 + 4], pr[o8 + 5], pr[o8 + 6], pr[o8 + 7]);
+      a_s = pack_bf16x8(ds[o8], ds[o8 + 1], ds[o8 + 2], ds[o8 + 3], ds[o8 + 4], ds[o8 + 5], ds[o8 + 6], ds[o8 + 7]);
+    };
     {
       constexpr int NP = 2 * DB;
       bf16x8 bdo[NP], bq[NP];
@@ -310,20 +309,31 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
         bdo[t] = join_tr(lds_read_tr(sd + row_a * D + ca), lds_read_tr(sd + row_b * D + cb));
         bq[t] = join_tr(lds_read_tr(sq + row_a * D + ca), lds_read_tr(sq + row_b * D + cb));
       };
-      rd(0);
-      rd(1);
+      bf16x8 ap0, as0, ap1, as1;
 #pragma unroll
-      for (int t = 0; t < NP; ++t) {
-        if (t + 2 < NP) rd(t + 2);
-        const int ks = t / DB, db = t % DB;
-        dv_acc[db] = mfma32(ap[ks], bdo[t], dv_acc[db]);
-        dk_acc[db] = mfma32(as[ks], bq[t], dk_acc[db]);
+      for (int db = 0; db < DB; ++db) rd(db);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pds(i);
+      pack_ks(0, ap0, as0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dv_acc[db] = mfma32(ap0, bdo[db], dv_acc[db]);
+        dk_acc[db] = mfma32(as0, bq[db], dk_acc[db]);
+        rd(DB + db);
+#pragma unroll
+        for (int i = 8 + db * (8 / DB); i < 8 + (db + 1) * (8 / DB); ++i) {
+          pds(i);
+          // pinned here: the IR optimisers would otherwise sink them to the pack below
+          asm volatile("" : "+v"(pr[i]), "+v"(ds[i]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+      pack_ks(1, ap1, as1);
 #pragma unroll
-      for (int t = 0; t < NP; ++t) {
-        if (t + 2 < NP) __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+      for (int db = 0; db < DB; ++db) {
+        dv_acc[db] = mfma32(ap1, bdo[DB + db], dv_acc[db]);
+        dk_acc[db] = mfma32(as1, bq[DB + db], dk_acc[db]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
