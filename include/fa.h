@@ -143,8 +143,9 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N);
  *   q, dout         [B, N, H, d] bf16, the forward's query and the upstream gradient
  *   k, v            [B, N, Hkv, d] bf16, the forward's keys and values
  *   o, lse          the forward's outputs for the same inputs (fa_fwd)
- *   dq              fp32 [B, N, H, d] (written): cleared by the call, then accumulated
- *                   with device atomics.
+ *   dq              fp32 [B, N, H, d] (written): each element written once, by a pass over
+ *                   query blocks that recomputes S and dP (the page accumulates dQ across
+ *                   key blocks with atomics instead; the result is the same sum).
  *   dk, dv          fp32 [B, N, Hkv, d] (written). With Hkv = H each element is written
  *                   once per key block; with Hkv < H a shared head receives the sum of
  *                   its group's gradients (cleared by the call, then added with device
@@ -152,9 +153,9 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N);
  *   workspace       >= fa_bwd_workspace_bytes(B, H, N) bytes of device memory.
  * Probabilities are recomputed from Q, K and the saved LSE as exp(s - LSE); the
  * gradient is dV = P^T dO, dS = P * (dO V^T - D), dQ = scale dS K, dK = scale dS^T Q.
- * Only FA_DTYPE_BF16 is accepted. The order of the atomic additions varies from
- * run to run, so dq (and dk, dv when grouped) are reproducible to rounding, not
- * bit for bit.
+ * Only FA_DTYPE_BF16 is accepted. With Hkv = H the outputs are the same bits run to
+ * run; with Hkv < H the order of the atomic additions into dk, dv varies, so those
+ * are reproducible to rounding, not bit for bit.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
            const void* dout, float* dq, float* dk, float* dv,
