@@ -45,6 +45,8 @@ def run_bwd(seed, B, N, H, d, causal):
     (2, 96, 2, 128, False),      # three query blocks per key block (odd step count)
     (1, 700, 2, 128, True),      # six key blocks, query-block counts of both parities
     (1, 513, 1, 64, True),
+    (1, 700, 8, 128, True),      # 8 heads: the XCD-ordered work decode, with a ragged last block
+    (1, 1000, 8, 64, False),
 ])
 def test_bwd_small(B, N, H, d, causal):
     (qb, kb, vb, gb), (dq, dk, dv) = run_bwd(4, B, N, H, d, causal)
