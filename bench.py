@@ -133,7 +133,8 @@ def cpu_baseline(target_s):
                       f"{len(os.sched_getaffinity(0))} cpus"}
 
 
-def extra_measurements(steps):
+def extra_measurements(steps, only=None):
+    """The secondary workloads; `only`, a set of names, restricts them (for profiler runs)."""
     import torch
     import io_aware_softmax_03_amd as fa
     from io_aware_softmax_03_amd import costs
@@ -141,142 +142,161 @@ def extra_measurements(steps):
     out = {}
     gen = torch.Generator(device="cuda")
 
-    # backward, B=4 H=16 N=4096 d=128 causal (preprocess + main kernel per call)
-    B, H, N, d = 4, 16, 4096, 128
-    gen.manual_seed(4)
-    q, k, v, g = (torch.randn((B, N, H, d), generator=gen, device="cuda", dtype=torch.bfloat16) for _ in range(4))
-    o, lse = fa.fwd(q, k, v, causal=True)
-    grads = tuple(torch.empty((B, N, H, d), dtype=torch.float32, device="cuda") for _ in range(3))
-    ws = torch.empty(fa.lib().fa_bwd_workspace_bytes(B, H, N), dtype=torch.uint8, device="cuda")
-    wall, ev, best = time_launches(lambda: fa.bwd(q, k, v, o, lse, g, causal=True, out=grads, workspace=ws),
-                                   steps, 3)
-    fl = costs.bwd_flops(B, H, N, d, True)
-    out["bwd_causal_b4_h16_n4096_d128"] = {
-        "ms": round(ev, 4), "tflops": round(fl / ev / 1e9, 2), "frac_mfma_peak": round(fl / ev / 1e9 / PEAK_BF16_TFLOPS, 4),
-        "flops_convention": "10*B*H*N^2*d/2 (five products)"}
-    del q, k, v, g, o, lse, grads, ws
-
-    # varlen forward: 16 sequences, lengths uniform in [128, 4096], H=32, d=64, causal, Q x4 on heads 16-31
-    lengths = synth.varlen_lengths(3, 16, 128, 4096).tolist()
-    cu = torch.tensor(synth.cu_seqlens_from_lengths(lengths), dtype=torch.int32, device="cuda")
-    T, H, d = sum(lengths), 32, 64
-    gen.manual_seed(3)
-    q, k, v = (torch.randn((T, H, d), generator=gen, device="cuda", dtype=torch.float32) for _ in range(3))
-    q[:, 16:] *= 4
-    q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
-    wall, ev, best = time_launches(lambda: fa.fwd_varlen(q, k, v, cu, max(lengths), causal=True), steps, 3)
-    fl = costs.varlen_fwd_flops(lengths, H, d, True)
-    out["varlen_causal_16seq_h32_d64"] = {"ms": round(ev, 4), "tflops": round(fl / ev / 1e9, 2),
-                                          "frac_mfma_peak": round(fl / ev / 1e9 / PEAK_BF16_TFLOPS, 4),
-                                          "total_tokens": T}
-    del q, k, v
-
-    # banded forwards (bf16, d=128, causal, bottom-right): chunked prefill of 2048 new
-    # queries against a 16384-key cache, and a 1024-key sliding window over 8192 tokens.
-    # Work counted as 4*d per visible (query, key) pair.
-    for name, B, H, Nq, Nk, left in (("fwd_chunked_prefill_b4_h16_q2048_k16384_d128", 4, 16, 2048, 16384, -1),
-                                     ("fwd_sliding_window1024_b2_h16_n8192_d128", 2, 16, 8192, 8192, 1024)):
-        d = 128
-        gen.manual_seed(10)
-        q = torch.randn((B, Nq, H, d), generator=gen, device="cuda", dtype=torch.bfloat16)
-        k, v = (torch.randn((B, Nk, H, d), generator=gen, device="cuda", dtype=torch.bfloat16) for _ in range(2))
-        o = torch.empty_like(q)
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda")
-        wall, ev, best = time_launches(lambda: fa.fwd_window(q, k, v, causal=True, window=(left, -1), out=(o, lse)),
+    def _bwd():
+        # backward, B=4 H=16 N=4096 d=128 causal (preprocess, dK/dV and dQ kernels per call)
+        B, H, N, d = 4, 16, 4096, 128
+        gen.manual_seed(4)
+        q, k, v, g = (torch.randn((B, N, H, d), generator=gen, device="cuda", dtype=torch.bfloat16) for _ in range(4))
+        o, lse = fa.fwd(q, k, v, causal=True)
+        grads = tuple(torch.empty((B, N, H, d), dtype=torch.float32, device="cuda") for _ in range(3))
+        ws = torch.empty(fa.lib().fa_bwd_workspace_bytes(B, H, N), dtype=torch.uint8, device="cuda")
+        wall, ev, best = time_launches(lambda: fa.bwd(q, k, v, o, lse, g, causal=True, out=grads, workspace=ws),
                                        steps, 3)
-        fl = costs.band_fwd_flops(B, H, Nq, Nk, d, True, left)
-        out[name] = {"ms": round(ev, 4), "tflops": round(fl / ev / 1e9, 2),
-                     "frac_mfma_peak": round(fl / ev / 1e9 / PEAK_BF16_TFLOPS, 4),
-                     "flops_convention": "4*d per visible (query, key) pair"}
-        del q, k, v, o, lse
+        fl = costs.bwd_flops(B, H, N, d, True)
+        out["bwd_causal_b4_h16_n4096_d128"] = {
+            "ms": round(ev, 4), "tflops": round(fl / ev / 1e9, 2), "frac_mfma_peak": round(fl / ev / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "flops_convention": "10*B*H*N^2*d/2 (five products)"}
+        del q, k, v, g, o, lse, grads, ws
 
-    # FP8 forward on the headline shape (causal B=2 H=16 N=8192 d=128), Q and K rotated:
-    # three quantization launches plus the attention launch per call
-    B, H, N, d = 2, 16, 8192, 128
-    gen.manual_seed(11)
-    q, k, v = (torch.randn((B, N, H, d), generator=gen, device="cuda", dtype=torch.bfloat16) for _ in range(3))
-    signs = torch.from_numpy(synth.rademacher_signs(11, d)).to("cuda")
-    ws = torch.empty(fa.lib().fa_fwd_fp8_workspace_bytes(B, H, H, N, d), dtype=torch.uint8, device="cuda")
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
-    wall, ev, best = time_launches(lambda: fa.fwd_fp8(q, k, v, signs=signs, causal=True, out=(o, lse), workspace=ws),
-                                   steps, 3)
-    fl = costs.fwd_flops(B, H, N, d, True)
-    out["fwd_fp8_causal_b2_h16_n8192_d128_rotated"] = {
-        "ms": round(ev, 4), "tflops": round(fl / ev / 1e9, 2),
-        "frac_fp8_mfma_peak": round(fl / ev / 1e9 / PEAK_FP8_TFLOPS, 4),
-        "flops_convention": "4*B*H*N^2*d/2, per call (quantization of Q, K, V included)"}
-    del q, k, v, o, lse, ws
 
-    # fp32 forward, B=1 H=1 N=256 d=64 (launch-latency bound)
-    gen.manual_seed(1)
-    q, k, v = (torch.randn((1, 256, 1, 64), generator=gen, device="cuda") for _ in range(3))
-    wall, ev, best = time_launches(lambda: fa.fwd(q, k, v), steps, 3)
-    out["fwd_f32_n256_d64"] = {"us": round(ev * 1e3, 2)}
-    del q, k, v
+    def _varlen():
+        # varlen forward: 16 sequences, lengths uniform in [128, 4096], H=32, d=64, causal, Q x4 on heads 16-31
+        lengths = synth.varlen_lengths(3, 16, 128, 4096).tolist()
+        cu = torch.tensor(synth.cu_seqlens_from_lengths(lengths), dtype=torch.int32, device="cuda")
+        T, H, d = sum(lengths), 32, 64
+        gen.manual_seed(3)
+        q, k, v = (torch.randn((T, H, d), generator=gen, device="cuda", dtype=torch.float32) for _ in range(3))
+        q[:, 16:] *= 4
+        q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
+        wall, ev, best = time_launches(lambda: fa.fwd_varlen(q, k, v, cu, max(lengths), causal=True), steps, 3)
+        fl = costs.varlen_fwd_flops(lengths, H, d, True)
+        out["varlen_causal_16seq_h32_d64"] = {"ms": round(ev, 4), "tflops": round(fl / ev / 1e9, 2),
+                                              "frac_mfma_peak": round(fl / ev / 1e9 / PEAK_BF16_TFLOPS, 4),
+                                              "total_tokens": T}
+        del q, k, v
 
-    # decode: B=64 H=32 L=32768 d=128, 64 splits (34 GB of bf16 cache)
-    B, H, L, d = 64, 32, 32768, 128
-    gen.manual_seed(5)
-    q = torch.randn((B, H, d), generator=gen, device="cuda", dtype=torch.bfloat16)
-    kc = torch.randn((B, L, H, d), generator=gen, device="cuda", dtype=torch.bfloat16)
-    vc = torch.randn((B, L, H, d), generator=gen, device="cuda", dtype=torch.bfloat16)
-    ws = torch.empty(fa.lib().fa_decode_workspace_bytes(B, H, d, 64), dtype=torch.uint8, device="cuda")
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
-    wall, ev, best = time_launches(lambda: fa.decode(q, kc, vc, num_splits=64, workspace=ws, out=(o, lse)),
-                                   max(3, steps // 2), 2)
-    nb = costs.decode_bytes(B, H, L, d)
-    out["decode_b64_h32_l32768_d128_s64"] = {"ms": round(ev, 4), "gbs": round(nb / ev / 1e6, 1),
-                                             "frac_hbm_peak": round(nb / ev / 1e6 / PEAK_HBM_GBS, 4),
-                                             "bytes_convention": "K and V caches read once + q + o"}
-    del q, kc, vc, ws
-    torch.cuda.empty_cache()
 
-    # grouped-query decode: 32 query heads over 8 key-value heads, L=32768, d=128; 32 splits
-    # (a sweep over 16..256 puts the grouped kernel's best at 32: with 8 key-value heads a
-    # 64-way split leaves each wave only 512 keys)
-    B, H, Hkv, L, d = 64, 32, 8, 32768, 128
-    gen.manual_seed(9)
-    q = torch.randn((B, H, d), generator=gen, device="cuda", dtype=torch.bfloat16)
-    kc = torch.randn((B, L, Hkv, d), generator=gen, device="cuda", dtype=torch.bfloat16)
-    vc = torch.randn((B, L, Hkv, d), generator=gen, device="cuda", dtype=torch.bfloat16)
-    ws = torch.empty(fa.lib().fa_decode_workspace_bytes(B, H, d, 32), dtype=torch.uint8, device="cuda")
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
-    wall, ev, best = time_launches(lambda: fa.decode(q, kc, vc, num_splits=32, workspace=ws, out=(o, lse)),
-                                   max(3, steps // 2), 2)
-    nb = costs.decode_bytes(B, Hkv, L, d) + 2.0 * B * (H - Hkv) * d * 2
-    out["decode_gqa_b64_h32_kv8_l32768_d128_s32"] = {
-        "ms": round(ev, 4), "gbs": round(nb / ev / 1e6, 1), "frac_hbm_peak": round(nb / ev / 1e6 / PEAK_HBM_GBS, 4),
-        "bytes_convention": "K and V caches (8 heads) read once + q + o (32 heads)"}
-    del q, kc, vc, ws
-    torch.cuda.empty_cache()
+    def _window():
+        # banded forwards (bf16, d=128, causal, bottom-right): chunked prefill of 2048 new
+        # queries against a 16384-key cache, and a 1024-key sliding window over 8192 tokens.
+        # Work counted as 4*d per visible (query, key) pair.
+        for name, B, H, Nq, Nk, left in (("fwd_chunked_prefill_b4_h16_q2048_k16384_d128", 4, 16, 2048, 16384, -1),
+                                         ("fwd_sliding_window1024_b2_h16_n8192_d128", 2, 16, 8192, 8192, 1024)):
+            d = 128
+            gen.manual_seed(10)
+            q = torch.randn((B, Nq, H, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+            k, v = (torch.randn((B, Nk, H, d), generator=gen, device="cuda", dtype=torch.bfloat16) for _ in range(2))
+            o = torch.empty_like(q)
+            lse = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda")
+            wall, ev, best = time_launches(lambda: fa.fwd_window(q, k, v, causal=True, window=(left, -1), out=(o, lse)),
+                                           steps, 3)
+            fl = costs.band_fwd_flops(B, H, Nq, Nk, d, True, left)
+            out[name] = {"ms": round(ev, 4), "tflops": round(fl / ev / 1e9, 2),
+                         "frac_mfma_peak": round(fl / ev / 1e9 / PEAK_BF16_TFLOPS, 4),
+                         "flops_convention": "4*d per visible (query, key) pair"}
+            del q, k, v, o, lse
 
-    # paged decode: B=64 H=32 d=128, 16-token pages scattered over the pool, lengths uniform
-    # in [16384, 32768], 32 splits (the sweep's best; sequences are up to half as long as
-    # the contiguous decode's)
-    B, H, d, P = 64, 32, 128, 16
-    seqlens = synth.varlen_lengths(8, B, 16384, 32768).tolist()
-    table, num_pages = synth.paged_layout(8, seqlens, P, 0)
-    gen.manual_seed(8)
-    q = torch.randn((B, H, d), generator=gen, device="cuda", dtype=torch.bfloat16)
-    kp = torch.randn((num_pages, P, H, d), generator=gen, device="cuda", dtype=torch.bfloat16)
-    vp = torch.randn((num_pages, P, H, d), generator=gen, device="cuda", dtype=torch.bfloat16)
-    tab = torch.from_numpy(table).to("cuda")
-    sl = torch.tensor(seqlens, dtype=torch.int32, device="cuda")
-    ws = torch.empty(fa.lib().fa_decode_workspace_bytes(B, H, d, 32), dtype=torch.uint8, device="cuda")
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
-    wall, ev, best = time_launches(
-        lambda: fa.decode_paged(q, kp, vp, tab, sl, num_splits=32, workspace=ws, out=(o, lse)),
-        max(3, steps // 2), 2)
-    nb = costs.decode_paged_bytes(seqlens, H, d)
-    out["decode_paged_b64_h32_p16_l16k_32k_d128_s32"] = {
-        "ms": round(ev, 4), "gbs": round(nb / ev / 1e6, 1), "frac_hbm_peak": round(nb / ev / 1e6 / PEAK_HBM_GBS, 4),
-        "tokens": int(sum(seqlens)), "bytes_convention": "valid K and V tokens read once + q + o"}
-    del q, kp, vp, ws
-    torch.cuda.empty_cache()
+
+    def _fp8():
+        # FP8 forward on the headline shape (causal B=2 H=16 N=8192 d=128), Q and K rotated:
+        # three quantization launches plus the attention launch per call
+        B, H, N, d = 2, 16, 8192, 128
+        gen.manual_seed(11)
+        q, k, v = (torch.randn((B, N, H, d), generator=gen, device="cuda", dtype=torch.bfloat16) for _ in range(3))
+        signs = torch.from_numpy(synth.rademacher_signs(11, d)).to("cuda")
+        ws = torch.empty(fa.lib().fa_fwd_fp8_workspace_bytes(B, H, H, N, d), dtype=torch.uint8, device="cuda")
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        wall, ev, best = time_launches(lambda: fa.fwd_fp8(q, k, v, signs=signs, causal=True, out=(o, lse), workspace=ws),
+                                       steps, 3)
+        fl = costs.fwd_flops(B, H, N, d, True)
+        out["fwd_fp8_causal_b2_h16_n8192_d128_rotated"] = {
+            "ms": round(ev, 4), "tflops": round(fl / ev / 1e9, 2),
+            "frac_fp8_mfma_peak": round(fl / ev / 1e9 / PEAK_FP8_TFLOPS, 4),
+            "flops_convention": "4*B*H*N^2*d/2, per call (quantization of Q, K, V included)"}
+        del q, k, v, o, lse, ws
+
+
+    def _f32():
+        # fp32 forward, B=1 H=1 N=256 d=64 (launch-latency bound)
+        gen.manual_seed(1)
+        q, k, v = (torch.randn((1, 256, 1, 64), generator=gen, device="cuda") for _ in range(3))
+        wall, ev, best = time_launches(lambda: fa.fwd(q, k, v), steps, 3)
+        out["fwd_f32_n256_d64"] = {"us": round(ev * 1e3, 2)}
+        del q, k, v
+
+
+    def _decode():
+        # decode: B=64 H=32 L=32768 d=128, 64 splits (34 GB of bf16 cache)
+        B, H, L, d = 64, 32, 32768, 128
+        gen.manual_seed(5)
+        q = torch.randn((B, H, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+        kc = torch.randn((B, L, H, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+        vc = torch.randn((B, L, H, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+        ws = torch.empty(fa.lib().fa_decode_workspace_bytes(B, H, d, 64), dtype=torch.uint8, device="cuda")
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+        wall, ev, best = time_launches(lambda: fa.decode(q, kc, vc, num_splits=64, workspace=ws, out=(o, lse)),
+                                       max(3, steps // 2), 2)
+        nb = costs.decode_bytes(B, H, L, d)
+        out["decode_b64_h32_l32768_d128_s64"] = {"ms": round(ev, 4), "gbs": round(nb / ev / 1e6, 1),
+                                                 "frac_hbm_peak": round(nb / ev / 1e6 / PEAK_HBM_GBS, 4),
+                                                 "bytes_convention": "K and V caches read once + q + o"}
+        del q, kc, vc, ws
+        torch.cuda.empty_cache()
+
+
+    def _decode_gqa():
+        # grouped-query decode: 32 query heads over 8 key-value heads, L=32768, d=128; 32 splits
+        # (a sweep over 16..256 puts the grouped kernel's best at 32: with 8 key-value heads a
+        # 64-way split leaves each wave only 512 keys)
+        B, H, Hkv, L, d = 64, 32, 8, 32768, 128
+        gen.manual_seed(9)
+        q = torch.randn((B, H, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+        kc = torch.randn((B, L, Hkv, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+        vc = torch.randn((B, L, Hkv, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+        ws = torch.empty(fa.lib().fa_decode_workspace_bytes(B, H, d, 32), dtype=torch.uint8, device="cuda")
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+        wall, ev, best = time_launches(lambda: fa.decode(q, kc, vc, num_splits=32, workspace=ws, out=(o, lse)),
+                                       max(3, steps // 2), 2)
+        nb = costs.decode_bytes(B, Hkv, L, d) + 2.0 * B * (H - Hkv) * d * 2
+        out["decode_gqa_b64_h32_kv8_l32768_d128_s32"] = {
+            "ms": round(ev, 4), "gbs": round(nb / ev / 1e6, 1), "frac_hbm_peak": round(nb / ev / 1e6 / PEAK_HBM_GBS, 4),
+            "bytes_convention": "K and V caches (8 heads) read once + q + o (32 heads)"}
+        del q, kc, vc, ws
+        torch.cuda.empty_cache()
+
+
+    def _decode_paged():
+        # paged decode: B=64 H=32 d=128, 16-token pages scattered over the pool, lengths uniform
+        # in [16384, 32768], 32 splits (the sweep's best; sequences are up to half as long as
+        # the contiguous decode's)
+        B, H, d, P = 64, 32, 128, 16
+        seqlens = synth.varlen_lengths(8, B, 16384, 32768).tolist()
+        table, num_pages = synth.paged_layout(8, seqlens, P, 0)
+        gen.manual_seed(8)
+        q = torch.randn((B, H, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+        kp = torch.randn((num_pages, P, H, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+        vp = torch.randn((num_pages, P, H, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+        tab = torch.from_numpy(table).to("cuda")
+        sl = torch.tensor(seqlens, dtype=torch.int32, device="cuda")
+        ws = torch.empty(fa.lib().fa_decode_workspace_bytes(B, H, d, 32), dtype=torch.uint8, device="cuda")
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+        wall, ev, best = time_launches(
+            lambda: fa.decode_paged(q, kp, vp, tab, sl, num_splits=32, workspace=ws, out=(o, lse)),
+            max(3, steps // 2), 2)
+        nb = costs.decode_paged_bytes(seqlens, H, d)
+        out["decode_paged_b64_h32_p16_l16k_32k_d128_s32"] = {
+            "ms": round(ev, 4), "gbs": round(nb / ev / 1e6, 1), "frac_hbm_peak": round(nb / ev / 1e6 / PEAK_HBM_GBS, 4),
+            "tokens": int(sum(seqlens)), "bytes_convention": "valid K and V tokens read once + q + o"}
+        del q, kp, vp, ws
+        torch.cuda.empty_cache()
+
+    for name, fn in [("bwd", _bwd), ("varlen", _varlen), ("window", _window), ("fp8", _fp8), ("f32", _f32), ("decode", _decode), ("decode_gqa", _decode_gqa), ("decode_paged", _decode_paged)]:
+        if only is None or name in only:
+            fn()
     return out
 
 
@@ -287,6 +307,9 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=1500)
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--extra-only", default=None,
+                    help="comma-separated secondary workloads to run (bwd, varlen, window, fp8, f32, decode, "
+                         "decode_gqa, decode_paged); for profiler runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-clocks", action="store_true",
                     help="skip reading the clock levels (rocm-smi); for runs under a profiler")
@@ -369,7 +392,8 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_extra:
         log("[bench] secondary workloads")
-        result["extra"] = extra_measurements(args.steps)
+        only = set(args.extra_only.split(",")) if args.extra_only else None
+        result["extra"] = extra_measurements(args.steps, only)
         log(f"[bench] extra: {json.dumps(result['extra'])}")
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (float64 oracle)")
