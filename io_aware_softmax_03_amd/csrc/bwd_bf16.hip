@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
   }
   const int h = bh % p.heads, b = bh / p.heads;
   const int N = p.seqlen;
-  const size_t rs = (size_t)p.heads * D;        // Q, dO, dQ row stride
+  const size_t rs = (size_t)p.heads * D;        // Q, dO row stride
   const size_t base = ((size_t)b * N * p.heads + h) * D;
   const size_t rsk = (size_t)p.kv_heads * D;    // K, V, dK, dV row stride
   const size_t base_kv = ((size_t)b * N * p.kv_heads + h / p.group) * D;
@@ -201,20 +201,20 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
     const unsigned bytes = (unsigned)(min(kBQ - 1, N - 1 - q0) * (int)rs + D) * 2u;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + base + (size_t)q0 * rs, bytes);
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.dout + base + (size_t)q0 * rs, bytes);
-    uint16_t* dq_ = decltype(bufc)::value ? s_q1 : s_q0;
-    uint16_t* dd_ = decltype(bufc)::value ? s_do1 : s_do0;
+    uint16_t* q_dst = decltype(bufc)::value ? s_q1 : s_q0;
+    uint16_t* do_dst = decltype(bufc)::value ? s_do1 : s_do0;
 #pragma unroll
     for (int it = 0; it < LOADS; ++it) {
       const int off = (wid * LOADS + it) * 1024;  // this wave-load's 1 KB slice of the tile
-      copy16_to_lds(rq, t_src[it], (char*)dq_ + off);
-      copy16_to_lds(rd, t_src[it], (char*)dd_ + off);
+      copy16_to_lds(rq, t_src[it], (char*)q_dst + off);
+      copy16_to_lds(rd, t_src[it], (char*)do_dst + off);
     }
     // the tile's base-2 LSE and D, 4 bytes per lane of wave 0 (rows past the end read 0: their
     // Q and dO rows are 0 too, so P = 1 there multiplies zero rows and dS = 0)
     if (wid == 0 && lane < kBQ) {
       const unsigned fb = (unsigned)min(kBQ, N - q0) * 4u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(lse_g + q0, fb), (lds_void*)(dq_ + QT), 4, 4u * lane, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(dlt_g + q0, fb), (lds_void*)(dq_ + QT + 2 * kBQ), 4, 4u * lane, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(lse_g + q0, fb), (lds_void*)(q_dst + QT), 4, 4u * lane, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(dlt_g + q0, fb), (lds_void*)(q_dst + QT + 2 * kBQ), 4, 4u * lane, 0, 0, 0);
     }
   };
 
