@@ -6,7 +6,8 @@
 //                   accumulators busy for `iters` rounds (operands in registers); the template
 //                   occupancy is one or two waves per SIMD.
 //   probe_mfma_exp  the same with one v_exp_f32 and four v_fma_f32 on independent values
-//                   issued between consecutive MFMAs (the forward kernel's per-score work).
+//                   issued between consecutive MFMAs (the forward kernel's per-score work),
+//                   at one wave per SIMD or with several waves sharing a SIMD.
 //   probe_read      streaming read of a buffer (16 bytes per lane, grid-stride).
 //   probe_copy      streaming copy between two buffers.
 //   probe_xcc       the XCD (XCC id hardware register) each workgroup runs on.
@@ -40,23 +41,26 @@ __global__ __launch_bounds__(256, OCC) void mfma_kernel(float* out, int iters, f
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
-__global__ __launch_bounds__(256, 1) void mfma_exp_kernel(float* out, int iters, float seed) {
+// NACC independent accumulators per wave: 8 at one wave per SIMD; 4 lets two or three waves
+// share a SIMD (the other waves' VALU work then runs beside a wave's MFMAs)
+template <int OCC, int NACC>
+__global__ __launch_bounds__(256, OCC) void mfma_exp_kernel(float* out, int iters, float seed) {
   bf16x8 a, b;
   for (int e = 0; e < 8; ++e) {
     a[e] = (__bf16)(seed + 0.001f * e);
     b[e] = (__bf16)(seed - 0.002f * e);
   }
-  f32x16 acc[8];
-  for (int k = 0; k < 8; ++k)
+  f32x16 acc[NACC];
+  for (int k = 0; k < NACC; ++k)
     for (int i = 0; i < 16; ++i) acc[k][i] = 0.f;
-  float x[8], y[8];
-  for (int k = 0; k < 8; ++k) {
+  float x[NACC], y[NACC];
+  for (int k = 0; k < NACC; ++k) {
     x[k] = seed * (k + 1) * 1e-3f;
     y[k] = 0.f;
   }
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < NACC; ++k) {
       acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[k], 0, 0, 0);
       // independent of the MFMAs: one exponential and four FMAs per MFMA
       y[k] += __builtin_amdgcn_exp2f(x[k]);
@@ -66,7 +70,7 @@ __global__ __launch_bounds__(256, 1) void mfma_exp_kernel(float* out, int iters,
     }
   }
   float s = 0.f;
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < NACC; ++k) {
     s += y[k];
     for (int i = 0; i < 16; ++i) s += acc[k][i];
   }
@@ -108,9 +112,13 @@ int probe_mfma(float* out, int grid, int iters, int waves_per_simd, void* stream
   return (int)hipGetLastError();
 }
 
-int probe_mfma_exp(float* out, int grid, int iters, void* stream) {
+// waves_per_simd 1: eight accumulators per wave; otherwise four (two or three waves per SIMD)
+int probe_mfma_exp(float* out, int grid, int iters, int waves_per_simd, void* stream) {
   if (!out || grid <= 0 || iters <= 0) return (int)hipErrorInvalidValue;
-  hipLaunchKernelGGL(mfma_exp_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, out, iters, 0.5f);
+  if (waves_per_simd == 1)
+    hipLaunchKernelGGL((mfma_exp_kernel<1, 8>), dim3(grid), dim3(256), 0, (hipStream_t)stream, out, iters, 0.5f);
+  else
+    hipLaunchKernelGGL((mfma_exp_kernel<2, 4>), dim3(grid), dim3(256), 0, (hipStream_t)stream, out, iters, 0.5f);
   return (int)hipGetLastError();
 }
 

@@ -22,7 +22,7 @@ def _lib():
     lib = ctypes.CDLL(LIB_PATH)
     P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.probe_mfma.argtypes = [P, I, I, I, P]
-    lib.probe_mfma_exp.argtypes = [P, I, I, P]
+    lib.probe_mfma_exp.argtypes = [P, I, I, I, P]
     lib.probe_read.argtypes = [P, Z, P, I, P]
     lib.probe_copy.argtypes = [P, P, Z, I, P]
     lib.probe_xcc.argtypes = [P, I, P]
@@ -62,17 +62,20 @@ def main():
     iters = 4000
     for label, fn_name, waves, grid in (("MFMA bf16 32x32x16, 1 wave/SIMD", "mfma", 1, 4 * cus),
                                         ("MFMA bf16 32x32x16, 3 waves/SIMD", "mfma", 2, 12 * cus),
-                                        ("MFMA + 1 exp + 4 FMA per MFMA, 1 wave/SIMD", "mfma_exp", 1, 4 * cus)):
+                                        ("MFMA + 1 exp + 4 FMA per MFMA, 1 wave/SIMD", "mfma_exp", 1, 4 * cus),
+                                        ("MFMA + 1 exp + 4 FMA per MFMA, several waves/SIMD", "mfma_exp", 2, 12 * cus)):
         out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
         if fn_name == "mfma":
             f = lambda: _check(lib.probe_mfma(out.data_ptr(), grid, iters, waves, stream), "probe_mfma")  # noqa: E731
         else:
-            f = lambda: _check(lib.probe_mfma_exp(out.data_ptr(), grid, iters, stream), "probe_mfma_exp")  # noqa: E731
+            f = lambda: _check(lib.probe_mfma_exp(out.data_ptr(), grid, iters, waves, stream), "probe_mfma_exp")  # noqa: E731
         # warm the clock with a longer run before timing
         _time(f, reps=3, warmup=20)
         ms = _time(f)
-        flops = grid * 4 * iters * 8 * MFMA_FLOP
-        rows.append((label, f"{flops / ms / 1e9:.0f} TFLOP/s", f"{grid} workgroups x 4 waves, {iters} rounds of 8 MFMAs"))
+        nacc = 4 if (fn_name == "mfma_exp" and waves != 1) else 8
+        flops = grid * 4 * iters * nacc * MFMA_FLOP
+        rows.append((label, f"{flops / ms / 1e9:.0f} TFLOP/s",
+                     f"{grid} workgroups x 4 waves, {iters} rounds of {nacc} MFMAs"))
 
     nbytes = 8 << 30
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
