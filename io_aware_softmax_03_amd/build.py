@@ -55,23 +55,6 @@ def _compile(src: str) -> str:
     return obj
 
 
-PROBES_SRC = os.path.join(PKG, "probes", "probes.hip")
-PROBES_LIB = os.path.join(PKG, "probes", "libfa_probes.so")
-
-
-def build_probes(verbose: bool = True) -> str:
-    """The hardware probes (not part of the attention library) into probes/libfa_probes.so."""
-    tmp = PROBES_LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-shared", PROBES_SRC, "-o", tmp]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {PROBES_SRC}:\n{res.stderr}")
-    os.replace(tmp, PROBES_LIB)
-    if verbose:
-        print(f"built {PROBES_LIB}")
-    return PROBES_LIB
-
-
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
@@ -90,5 +73,4 @@ def build(verbose: bool = True) -> str:
 
 if __name__ == "__main__":
     build()
-    build_probes()
     sys.exit(0)
