@@ -34,6 +34,7 @@ METRIC = "attention fwd TFLOP/s (bf16 causal N=8192 d=128) and % of MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
 PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS  # dense e4m3 matrix-core peak (5.0 PFLOP/s)
+SETTLE_S = 0.25  # untimed calls before each secondary workload's warm-up
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_causal_b2_h16_n8192_d128_traffic.json")
 FWD_SOURCE = os.path.join(ROOT, "io_aware_softmax_03_amd", "csrc", "fwd_bf16.hip")
 
@@ -47,10 +48,18 @@ def source_digest(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def time_launches(fn, steps, warmup):
+def time_launches(fn, steps, warmup, settle_s=0.0):
     """Warm up, then time `steps` calls: wall clock between synchronisations, and per-call
-    HIP event pairs recorded on the stream the kernels are launched on."""
+    HIP event pairs recorded on the stream the kernels are launched on. With settle_s > 0,
+    calls run untimed for about that many seconds before the `warmup` calls (the secondary
+    workloads use it: the GPU clock rises over tens of milliseconds of sustained load)."""
     import torch
+    if settle_s > 0:
+        t_end = time.perf_counter() + settle_s
+        while time.perf_counter() < t_end:
+            for _ in range(8):
+                fn()
+            torch.cuda.synchronize()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -67,26 +76,6 @@ def time_launches(fn, steps, warmup):
     ev = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     time_launches.last_median = sorted(ev)[len(ev) // 2]
     return wall_ms, sum(ev) / len(ev), min(ev)
-
-
-def clocks_under_load(fn, launches=400):
-    """GPU clock levels read with rocm-smi while `launches` more calls (untimed) run."""
-    import subprocess
-    import torch
-    for _ in range(launches):
-        fn()
-    try:
-        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20).stdout
-    except (OSError, subprocess.SubprocessError):
-        out = ""
-    torch.cuda.synchronize()
-    res = {}
-    for line in out.splitlines():
-        low = line.lower()
-        for key in ("sclk", "mclk", "fclk"):
-            if key + " clock level" in low and "(" in line:
-                res[key + "_mhz"] = line.rsplit("(", 1)[1].split(")")[0].lower().replace("mhz", "").strip()
-    return res
 
 
 def traffic_from_profile():
@@ -151,7 +140,7 @@ def extra_measurements(steps, only=None):
         grads = tuple(torch.empty((B, N, H, d), dtype=torch.float32, device="cuda") for _ in range(3))
         ws = torch.empty(fa.lib().fa_bwd_workspace_bytes(B, H, N), dtype=torch.uint8, device="cuda")
         wall, ev, best = time_launches(lambda: fa.bwd(q, k, v, o, lse, g, causal=True, out=grads, workspace=ws),
-                                       steps, 3)
+                                       steps, 3, SETTLE_S)
         fl = costs.bwd_flops(B, H, N, d, True)
         out["bwd_causal_b4_h16_n4096_d128"] = {
             "ms": round(ev, 4), "tflops": round(fl / ev / 1e9, 2), "frac_mfma_peak": round(fl / ev / 1e9 / PEAK_BF16_TFLOPS, 4),
@@ -168,7 +157,7 @@ def extra_measurements(steps, only=None):
         q, k, v = (torch.randn((T, H, d), generator=gen, device="cuda", dtype=torch.float32) for _ in range(3))
         q[:, 16:] *= 4
         q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
-        wall, ev, best = time_launches(lambda: fa.fwd_varlen(q, k, v, cu, max(lengths), causal=True), steps, 3)
+        wall, ev, best = time_launches(lambda: fa.fwd_varlen(q, k, v, cu, max(lengths), causal=True), steps, 3, SETTLE_S)
         fl = costs.varlen_fwd_flops(lengths, H, d, True)
         out["varlen_causal_16seq_h32_d64"] = {"ms": round(ev, 4), "tflops": round(fl / ev / 1e9, 2),
                                               "frac_mfma_peak": round(fl / ev / 1e9 / PEAK_BF16_TFLOPS, 4),
@@ -189,7 +178,7 @@ def extra_measurements(steps, only=None):
             o = torch.empty_like(q)
             lse = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda")
             wall, ev, best = time_launches(lambda: fa.fwd_window(q, k, v, causal=True, window=(left, -1), out=(o, lse)),
-                                           steps, 3)
+                                           steps, 3, SETTLE_S)
             fl = costs.band_fwd_flops(B, H, Nq, Nk, d, True, left)
             out[name] = {"ms": round(ev, 4), "tflops": round(fl / ev / 1e9, 2),
                          "frac_mfma_peak": round(fl / ev / 1e9 / PEAK_BF16_TFLOPS, 4),
@@ -208,7 +197,7 @@ def extra_measurements(steps, only=None):
         o = torch.empty_like(q)
         lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
         wall, ev, best = time_launches(lambda: fa.fwd_fp8(q, k, v, signs=signs, causal=True, out=(o, lse), workspace=ws),
-                                       steps, 3)
+                                       steps, 3, SETTLE_S)
         fl = costs.fwd_flops(B, H, N, d, True)
         out["fwd_fp8_causal_b2_h16_n8192_d128_rotated"] = {
             "ms": round(ev, 4), "tflops": round(fl / ev / 1e9, 2),
@@ -221,7 +210,7 @@ def extra_measurements(steps, only=None):
         # fp32 forward, B=1 H=1 N=256 d=64 (launch-latency bound)
         gen.manual_seed(1)
         q, k, v = (torch.randn((1, 256, 1, 64), generator=gen, device="cuda") for _ in range(3))
-        wall, ev, best = time_launches(lambda: fa.fwd(q, k, v), steps, 3)
+        wall, ev, best = time_launches(lambda: fa.fwd(q, k, v), steps, 3, SETTLE_S)
         out["fwd_f32_n256_d64"] = {"us": round(ev * 1e3, 2)}
         del q, k, v
 
@@ -237,7 +226,7 @@ def extra_measurements(steps, only=None):
         o = torch.empty_like(q)
         lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
         wall, ev, best = time_launches(lambda: fa.decode(q, kc, vc, num_splits=64, workspace=ws, out=(o, lse)),
-                                       max(3, steps // 2), 2)
+                                       max(3, steps // 2), 2, SETTLE_S)
         nb = costs.decode_bytes(B, H, L, d)
         out["decode_b64_h32_l32768_d128_s64"] = {"ms": round(ev, 4), "gbs": round(nb / ev / 1e6, 1),
                                                  "frac_hbm_peak": round(nb / ev / 1e6 / PEAK_HBM_GBS, 4),
@@ -259,7 +248,7 @@ def extra_measurements(steps, only=None):
         o = torch.empty_like(q)
         lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
         wall, ev, best = time_launches(lambda: fa.decode(q, kc, vc, num_splits=32, workspace=ws, out=(o, lse)),
-                                       max(3, steps // 2), 2)
+                                       max(3, steps // 2), 2, SETTLE_S)
         nb = costs.decode_bytes(B, Hkv, L, d) + 2.0 * B * (H - Hkv) * d * 2
         out["decode_gqa_b64_h32_kv8_l32768_d128_s32"] = {
             "ms": round(ev, 4), "gbs": round(nb / ev / 1e6, 1), "frac_hbm_peak": round(nb / ev / 1e6 / PEAK_HBM_GBS, 4),
@@ -286,7 +275,7 @@ def extra_measurements(steps, only=None):
         lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
         wall, ev, best = time_launches(
             lambda: fa.decode_paged(q, kp, vp, tab, sl, num_splits=32, workspace=ws, out=(o, lse)),
-            max(3, steps // 2), 2)
+            max(3, steps // 2), 2, SETTLE_S)
         nb = costs.decode_paged_bytes(seqlens, H, d)
         out["decode_paged_b64_h32_p16_l16k_32k_d128_s32"] = {
             "ms": round(ev, 4), "gbs": round(nb / ev / 1e6, 1), "frac_hbm_peak": round(nb / ev / 1e6 / PEAK_HBM_GBS, 4),
@@ -303,7 +292,6 @@ def extra_measurements(steps, only=None):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    # the default warm-up (about a second of launches) lets the GPU clock settle before timing
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=1500)
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
@@ -311,8 +299,6 @@ def main():
                     help="comma-separated secondary workloads to run (bwd, varlen, window, fp8, f32, decode, "
                          "decode_gqa, decode_paged); for profiler runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-clocks", action="store_true",
-                    help="skip reading the clock levels (rocm-smi); for runs under a profiler")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (untimed), so that a counter "
@@ -336,6 +322,17 @@ def main():
         log(f"[bench] calibration copy: {n} bytes read, {n} bytes written")
         del src, dst
 
+    # The secondary workloads run first (each after a short untimed settle of its own), so the
+    # headline's W warm-up steps and K timed steps follow sustained GPU load rather than an
+    # idle GPU whose clock is still rising.
+    extra = None
+    if not args.no_extra:
+        log("[bench] secondary workloads")
+        only = set(args.extra_only.split(",")) if args.extra_only else None
+        extra = extra_measurements(args.steps, only)
+        log(f"[bench] extra: {json.dumps(extra)}")
+        torch.cuda.empty_cache()
+
     B, H, N, d = 2, 16, 8192, 128
     log(f"[bench] headline: causal bf16 forward B={B} H={H} N={N} d={d}")
     gen = torch.Generator(device="cuda")
@@ -346,7 +343,6 @@ def main():
     step = lambda: fa.fwd(q, k, v, causal=True, out=(o, lse))  # noqa: E731
     wall_ms, kern_ms, kern_min = time_launches(step, args.steps, args.warmup)
     kern_median = time_launches.last_median
-    clocks = None if args.no_clocks else clocks_under_load(step)
     flops = costs.fwd_flops(B, H, N, d, True)
     value = flops / (wall_ms * 1e-3) / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
@@ -376,25 +372,12 @@ def main():
                      "kernel": "fwd_bf16_kernel<128, causal, dense>", "launch_ms": round(kern_ms, 4),
                      "launch_ms_median": round(kern_median, 4), "launch_ms_min": round(kern_min, 4)},
         "device": {"name": prop.name, "gcn_arch": getattr(prop, "gcnArchName", ""),
-                   "cus": prop.multi_processor_count, "clocks_during_headline": clocks},
+                   "cus": prop.multi_processor_count},
     }
-    # the same fraction against the dense bf16 peak at the shader clock read during the run
-    # (256 CUs x 4096 FLOP per clock): the published peak assumes 2.4 GHz
-    try:
-        sclk = float(clocks["sclk_mhz"]) if clocks else None
-    except (KeyError, TypeError, ValueError):
-        sclk = None
-    if sclk:
-        peak_at_clock = prop.multi_processor_count * 4096 * sclk * 1e6 / 1e12
-        result["roofline"]["peak_at_measured_sclk"] = round(peak_at_clock, 1)
-        result["roofline"]["frac_at_measured_sclk"] = round(achieved / peak_at_clock, 4)
+    if extra is not None:
+        result["extra"] = extra
     del q, k, v, o, lse
     torch.cuda.empty_cache()
-    if not args.no_extra:
-        log("[bench] secondary workloads")
-        only = set(args.extra_only.split(",")) if args.extra_only else None
-        result["extra"] = extra_measurements(args.steps, only)
-        log(f"[bench] extra: {json.dumps(result['extra'])}")
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (float64 oracle)")
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

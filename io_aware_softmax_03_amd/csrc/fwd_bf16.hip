@@ -3,11 +3,12 @@
 // Method ("FlashAttention: IO-aware exact attention", "Tile decomposition" and "Online
 // softmax"; "FlashAttention-2 and -3", "Fewer non-matmul FLOPs", "Parallelism over the
 // sequence", "Split the queries, not the keys"):
-//   * one workgroup of four waves per (query block of 256 rows, batch*head); the query block
-//     stays in registers while 32-key blocks of K and V stream through LDS (double buffered);
-//   * each wave owns 64 whole query rows (two groups of 32), so the running max, running sum
-//     and output accumulator of a row never leave the wave, and every K or V operand read
-//     from LDS feeds two MFMAs (one per query group);
+//   * one workgroup of eight waves per (query block of 256 rows, batch*head), two waves per
+//     SIMD; the query block stays in registers while 32-key blocks of K and V stream through
+//     LDS (double buffered) and are shared by the eight waves;
+//   * each wave owns 32 whole query rows, so the running max, running sum and output
+//     accumulator of a row never leave the wave (the code is written for NG = kQW / 32
+//     query groups per wave, each K or V operand read from LDS feeding NG MFMAs);
 //   * scores are computed transposed, S^T = K Q^T, so the 32 keys x 32 queries MFMA output
 //     leaves one query per lane (16 scores, the other 16 in the lane 32 away) and the row
 //     max / row sum are in-lane plus one swap between wave halves;
@@ -26,21 +27,25 @@
 //     row's lowest and last row's highest visible key, and with a window each wave starts
 //     at its own first block;
 //   * grouped-query attention: query head h reads key-value head h / (H / Hkv).
-// gfx950 specifics: one wave per SIMD (512 registers: output accumulators and score tiles in
-// VGPRs, the Q operands in AGPRs); K and V tiles go from global memory straight into LDS
-// (buffer loads with an LDS destination, lane i -> bytes 16i of a wave's 1 KB slice), each
-// lane picking the source chunk that lands it at its swizzled position. Within a wave the
-// loop is a three-stage software pipeline: while the MFMAs of the next block's scores and
-// of the previous block's P V run, the VALU turns this block's scores into probabilities.
+// gfx950 specifics: two waves per SIMD (256 registers each: output accumulators, Q
+// operands and score tiles all in VGPRs), so one wave's exponentials and LDS reads issue
+// beside the other wave's MFMAs (a lone wave issues a VALU instruction only every ~6 cycles,
+// an exponential every ~12, against 32 cycles per MFMA); K and V tiles go from global memory
+// straight into LDS (buffer loads with an LDS destination, lane i -> bytes 16i of a wave's
+// 1 KB slice), each lane picking the source chunk that lands it at its swizzled position.
+// Within a wave the loop is a three-stage software pipeline: while the MFMAs of the next
+// block's scores and of the previous block's P V run, the VALU turns this block's scores
+// into probabilities.
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
 namespace fa {
 namespace {
 
-constexpr int kBC = 32;  // keys per streamed block
-constexpr int kNW = 4;   // waves per workgroup
-constexpr int kQW = 64;  // query rows per wave
+constexpr int kBC = 32;       // keys per streamed block
+constexpr int kNW = 8;        // waves per workgroup (two per SIMD)
+constexpr int kQW = 32;       // query rows per wave
+constexpr int NG = kQW / 32;  // 32-row query groups per wave
 constexpr int kBR = kNW * kQW;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units, for a wave's first block: P <= 256
 // Bound on P after the first block. The result is exact for any pivot; the bound only keeps
@@ -114,8 +119,10 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
   constexpr int CH = D / 8;                  // 16-byte chunks per row
   constexpr int TILE_B = kBC * D * 2;        // bytes of one K or V tile
   constexpr int ROWS_PER_KB = 1024 / (2 * D);
-  constexpr int LOADS = TILE_B / 1024 / kNW; // 1 KB wave-loads per tile per wave
-  static_assert(TILE_B % (1024 * kNW) == 0, "tile must split evenly over waves");
+  // 1 KB wave-loads per tile: LOADS per wave for the first CPW waves (the others copy nothing)
+  constexpr int CPW = TILE_B / 1024 < kNW ? TILE_B / 1024 : kNW;
+  constexpr int LOADS = TILE_B / 1024 / CPW;
+  static_assert(TILE_B % (1024 * CPW) == 0, "tile must split evenly over the copying waves");
   static_assert(KS == 2, "the score layout below assumes 32-key blocks");
 
   // Double-buffered K and V tiles, as four separate LDS objects: every access names its
@@ -197,19 +204,18 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
     // ---- Q fragments (B operand of S^T = K Q^T): lane holds, for query group g, row
     // qw + 32g + r, dims 16kk + 8hh .. +7. Rows past the end read the last row (finite
     // values, never stored).
-    bf16x8 qf[2][KK];
+    bf16x8 qf[NG][KK];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < NG; ++g) {
       const uint16_t* qrow = qg + (size_t)min(qw + 32 * g + r, L - 1) * rs + 8 * hh;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) qf[g][kk] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * kk));
     }
-    // the Q operands live in AGPRs (MFMA reads its A and B operands from either file), leaving
-    // the VGPRs to the scores and probabilities the VALU works on
+    // the Q operands are pinned here, before the block loop, so the loads are not sunk into it
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+    for (int g = 0; g < NG; ++g)
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+a"(qf[g][kk]));
+      for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(qf[g][kk]));
 
     // key blocks t0 .. t0 + ntiles - 1 of this query block: from the block holding the first
     // row's lowest visible key to the one holding the last row's highest (blocks outside
@@ -251,8 +257,10 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
       const unsigned bytes = (unsigned)(min(kBC - 1, Lk - 1 - k0) * rsk + D) * 2u;
       const __amdgpu_buffer_rsrc_t src = make_rsrc((IS_K ? kg : vg) + (size_t)k0 * rsk, bytes);
       char* dst = (IS_K ? kbuf(bufc) : vbuf(bufc)) + wid * LOADS * 1024;
+      if (CPW == kNW || wid < CPW) {
 #pragma unroll
-      for (int it = 0; it < LOADS; ++it) copy16_to_lds(src, IS_K ? k_src[it] : v_src[it], dst + it * 1024);
+        for (int it = 0; it < LOADS; ++it) copy16_to_lds(src, IS_K ? k_src[it] : v_src[it], dst + it * 1024);
+      }
     };
 
     // ---- per-lane LDS operand offsets, bytes within a tile buffer
@@ -282,16 +290,22 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
     // per query group: pivot (log2 units of scaled score, shared by both wave halves), this
     // lane's half of the running fp32 sum of P (for the LSE), and of the sum of P as rounded
     // to bf16 for the MFMA (normalises O)
-    float m_ref[2] = {-1e30f, -1e30f};
-    float l_part[2] = {0.f, 0.f};
-    float lr_part[2] = {0.f, 0.f};
+    float m_ref[NG], l_part[NG], lr_part[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      m_ref[g] = -1e30f;
+      l_part[g] = 0.f;
+      lr_part[g] = 0.f;
+    }
     // Sums of the rounded P formed on the matrix core: v_mfma_f32_16x16x32_bf16 with a 0/1
     // selector as A and a P^T operand as B. Read as a 16x16x32 B operand, the P^T register of
     // lane l is column l%16, k-block l/16; blocks 0 and 2 hold query l%16 (both wave halves),
     // blocks 1 and 3 query l%16 + 16. Selector rows 0-7 take blocks 0 and 2, rows 8-15 blocks
     // 1 and 3, so every output row is a complete 16-key sum; lane l ends up holding the sum
     // of query q16(l) = l%16 + 16*(l/32) (four equal copies).
-    f32x4 lsum[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    f32x4 lsum[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) lsum[g] = f32x4{0.f, 0.f, 0.f, 0.f};
     bf16x8 sel;
     {
       const __bf16 one = (((lane >> 4) & 1) == ((lane & 15) >= 8)) ? (__bf16)1.0f : (__bf16)0.0f;
@@ -299,9 +313,9 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
       for (int e = 0; e < 8; ++e) sel[e] = one;
     }
     const int lane_q16 = (lane & 15) + 16 * (lane >> 5);  // query whose sum lane holds in lsum
-    f32x16 oacc[2][DB];
+    f32x16 oacc[NG][DB];
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+    for (int g = 0; g < NG; ++g)
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -314,9 +328,9 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
       return (CAUSAL && k0 + kBC - 1 > qw + p.hi_off) || (k0 + kBC > Lk) ||
              (WINDOW && k0 < qw + kQW - 1 + p.lo_off);
     };
-    auto mask = [&](f32x16 (&s)[2], int k0) {
+    auto mask = [&](f32x16 (&s)[NG], int k0) {
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
+      for (int g = 0; g < NG; ++g) {
         const int row = qw + 32 * g + r;
         const int lim = CAUSAL ? min(row + p.hi_off, Lk - 1) : Lk - 1;  // last visible key
         const int low = row + p.lo_off;                                  // first visible key
@@ -353,11 +367,13 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
     };
     // Before a wave's first block: move a group's pivot when the block maximum exceeds it by
     // more than the threshold, rescaling the P block not yet multiplied into O as well.
-    auto repivot = [&](const float (&mt)[2], bf16x8 (&pend)[2][KS]) {
-      const bool up = mt[0] > m_ref[0] + kRescaleThreshold || mt[1] > m_ref[1] + kRescaleThreshold;
+    auto repivot = [&](const float (&mt)[NG], bf16x8 (&pend)[NG][KS]) {
+      bool up = false;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) up = up || mt[g] > m_ref[g] + kRescaleThreshold;
       if (wave_any(up)) {
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
+        for (int g = 0; g < NG; ++g) {
           const float m_new = fmaxf(m_ref[g], mt[g]);
           const float alpha = exp2_fast(m_ref[g] - m_new);
           m_ref[g] = m_new;
@@ -368,25 +384,20 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
       }
     };
     // running sums of the bf16-rounded P the MFMA uses
-    auto rsums = [&](const bf16x8 (&pb)[2][KS]) {
+    auto rsums = [&](const bf16x8 (&pb)[NG][KS]) {
 #pragma unroll
-      for (int g = 0; g < 2; ++g)
+      for (int g = 0; g < NG; ++g)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) lr_part[g] = sum_bf16x8(pb[g][ks], lr_part[g]);
     };
     // S^T = K Q^T for both query groups from K buffer BUF
-    auto qk = [&](f32x16 (&s)[2], auto bufc) {
+    auto qk = [&](f32x16 (&s)[NG], auto bufc) {
       const char* kb = kbuf(bufc);
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(kb + k_off[kk]));
-        if (kk == 0) {
-          s[0] = mfma32(a, qf[0][0], f32x16{});
-          s[1] = mfma32(a, qf[1][0], f32x16{});
-        } else {
-          s[0] = mfma32(a, qf[0][kk], s[0]);
-          s[1] = mfma32(a, qf[1][kk], s[1]);
-        }
+#pragma unroll
+        for (int g = 0; g < NG; ++g) s[g] = mfma32(a, qf[g][kk], kk == 0 ? f32x16{} : s[g]);
       }
     };
     // A P block with a value above kPMax (a lane's sum of its 16 values says so, inf
@@ -395,12 +406,12 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
     // overwritten by then), the pivot moves to the block's maximum, and the block's P (fp32
     // sums into bs, bf16 operands into pb) is redone with it; the factor O and the running sums
     // must be multiplied by goes to alpha.
-    auto rescue = [&](int k0, bf16x8 (&pb)[2][KS], float (&bs)[2], float (&alpha)[2]) {
+    auto rescue = [&](int k0, bf16x8 (&pb)[NG][KS], float (&bs)[NG], float (&alpha)[NG]) {
       const uint16_t* krow = kg + (size_t)min(k0 + r, Lk - 1) * rsk + 8 * hh;
       // one query group at a time and one K operand at a time (scheduling barriers keep the
       // loads from being hoisted), so this path needs few registers beyond the step's own
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
+      for (int g = 0; g < NG; ++g) {
         f32x16 sg[1];
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
@@ -440,15 +451,14 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
       return join_tr(lds_read_tr((const uint16_t*)va), lds_read_tr((const uint16_t*)(va + 8 * D * 2)));
     };
     // O^T += V^T P^T for k-step ks of both query groups
-    auto pv_step = [&](const bf16x8 (&va)[DB], const bf16x8 (&pb)[2][KS], int ks) {
+    auto pv_step = [&](const bf16x8 (&va)[DB], const bf16x8 (&pb)[NG][KS], int ks) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        oacc[0][db] = mfma32(va[db], pb[0][ks], oacc[0][db]);
-        oacc[1][db] = mfma32(va[db], pb[1][ks], oacc[1][db]);
-      }
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < NG; ++g) oacc[g][db] = mfma32(va[db], pb[g][ks], oacc[g][db]);
     };
     // the last P block of a wave, multiplied into O on its own
-    auto pv_tail = [&](const bf16x8 (&pb)[2][KS], auto bufc) {
+    auto pv_tail = [&](const bf16x8 (&pb)[NG][KS], auto bufc) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         bf16x8 va[DB];
@@ -484,19 +494,22 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
 #pragma unroll
       for (int o = tid * 16; o < TILE_B; o += kNW * 64 * 16) *(u32x4*)(v_lds1 + o) = z;
     }
-    f32x16 sA[2], sB[2];
-    bf16x8 pA[2][KS], pB[2][KS];
+    f32x16 sA[NG], sB[NG];
+    bf16x8 pA[NG][KS], pB[NG][KS];
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+    for (int g = 0; g < NG; ++g)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) pB[g][ks] = bf16x8{};
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (ws == 0 && wtiles > 0) {
       qk(sA, B0());
-      asm volatile("" : "+v"(sA[0]), "+v"(sA[1]));
+#pragma unroll
+      for (int g = 0; g < NG; ++g) asm volatile("" : "+v"(sA[g]));
       if (edge(kb0)) mask(sA, kb0);
-      const float mt[2] = {rowmax(sA[0]), rowmax(sA[1])};
+      float mt[NG];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) mt[g] = rowmax(sA[g]);
       repivot(mt, pB);
     }
     __syncthreads();  // every wave is done with K(0)
@@ -512,10 +525,16 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
     // rounded sums of P(j-1), and LDS reads a few slots ahead of the MFMA that consumes them.
     // P(j) is formed with the current pivot; no row maximum is taken. The lane sums of P(j)
     // bound its values: when one exceeds kPMax (rare) the block is redone with a new pivot.
-    constexpr int NQK = 2 * KK;               // score MFMAs (both query groups)
-    constexpr int NSLOT = NQK + 2 * KS * DB;  // + P V MFMAs
-    constexpr int VPS = 32 / NSLOT;           // probabilities per slot (1 for D=128, 2 for D=64)
-    static_assert(32 % NSLOT == 0, "slot plan");
+    constexpr int NQK = NG * KK;               // score MFMAs (all query groups)
+    constexpr int NSLOT = NQK + NG * KS * DB;  // + P V MFMAs
+    constexpr int NV = 16 * NG;                // probabilities of a block per lane
+    constexpr int VPS = NV / NSLOT;            // probabilities per slot (1 for D=128, 2 for D=64)
+    static_assert(NV % NSLOT == 0, "slot plan");
+    // LDS operand reads run a few slots ahead of the MFMAs that consume them (a sweep of both
+    // distances over 2..8 slots changed the headline time by less than 1%)
+    constexpr int KAH = 4;                     // K operand reads, slots ahead of their MFMA
+    constexpr int KR = KAH / NG + 1;           // K operands in flight (ring)
+    constexpr int VAH = NG == 1 ? 4 : 6;       // V operand reads, slots ahead of their MFMA
     // slot plan (slot -1 is the preamble before the first MFMA, slot NSLOT the tail after the last)
     auto fma_slot = [](int v) { return v / VPS - 1; };
     auto exp_slot = [](int v) { return v / VPS; };
@@ -524,26 +543,28 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
     // the row-sum MFMAs need no LDS operand: they fill the matrix pipe at the start of the
     // step while the first K operands are read
     auto lsum_slot = [](int k) { return -1 + 0 * k; };
-    auto kread_slot = [](int kk) { return kk < 3 ? -1 : 2 * kk - 4; };
+    auto kread_slot = [](int kk) { return kk * NG - KAH < -1 ? -1 : kk * NG - KAH; };
     auto vread_slot = [](int ks, int db, int hf) {
-      const int t = NQK + 2 * DB * ks + 2 * db - 6 + hf;
+      const int t = NQK + (ks * DB + db) * NG - VAH + hf;
       return t < -1 ? -1 : t;
     };
 
     auto step = [&](auto phase, int j) {
       constexpr int PH = decltype(phase)::value;
       constexpr bool ODD = PH & 1;
-      f32x16(&c)[2] = ODD ? sB : sA;       // S(j)
-      f32x16(&n)[2] = ODD ? sA : sB;       // S(j+1)
-      bf16x8(&pc)[2][KS] = ODD ? pB : pA;  // P(j)
-      bf16x8(&pp)[2][KS] = ODD ? pA : pB;  // P(j-1)
+      f32x16(&c)[NG] = ODD ? sB : sA;       // S(j)
+      f32x16(&n)[NG] = ODD ? sA : sB;       // S(j+1)
+      bf16x8(&pc)[NG][KS] = ODD ? pB : pA;  // P(j)
+      bf16x8(&pp)[NG][KS] = ODD ? pA : pB;  // P(j-1)
       const char* kb = kbuf(std::integral_constant<int, PH + 1>());  // K(j+1)
       const char* vb = vbuf(std::integral_constant<int, PH + 1>());  // V(j-1)
-      const float mneg[2] = {-m_ref[0], -m_ref[1]};
-      bf16x8 ka[3];
+      float mneg[NG];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) mneg[g] = -m_ref[g];
+      bf16x8 ka[KR];
       i16x4 vlo[KS][DB], vhi[KS][DB];
-      float acc[2][4];  // four partial fp32 sums of P(j) per query group
-      bf16x2 pr[16];    // P(j) pairs: pair q holds values 2q, 2q+1 (value v = 16g + i is c[g][i])
+      float acc[NG][4];  // four partial fp32 sums of P(j) per query group
+      bf16x2 pr[NV / 2]; // P(j) pairs: pair q holds values 2q, 2q+1 (value v = 16g + i is c[g][i])
 
       auto slot = [&](auto tc) {
         constexpr int t = decltype(tc)::value;
@@ -551,7 +572,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
         // LDS reads
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
-          if (kread_slot(kk) == t) ka[kk % 3] = __builtin_bit_cast(bf16x8, *(const u32x4*)(kb + k_off[kk]));
+          if (kread_slot(kk) == t) ka[kk % KR] = __builtin_bit_cast(bf16x8, *(const u32x4*)(kb + k_off[kk]));
 #pragma unroll
         for (int x = 0; x < KS * DB * 2; ++x) {
           const int ks = x / (2 * DB), db = (x / 2) % DB, hf = x % 2;
@@ -563,22 +584,22 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
         }
         // the slot's MFMA
         if constexpr (t >= 0 && t < NQK) {
-          constexpr int kk = t / 2, g = t % 2;
-          n[g] = mfma32(ka[kk % 3], qf[g][kk], kk == 0 ? f32x16{} : n[g]);
+          constexpr int kk = t / NG, g = t % NG;
+          n[g] = mfma32(ka[kk % KR], qf[g][kk], kk == 0 ? f32x16{} : n[g]);
         } else if constexpr (t >= NQK && t < NSLOT) {
-          constexpr int u = t - NQK, ks = u / (2 * DB), db = (u / 2) % DB, g = u % 2;
+          constexpr int u = t - NQK, ks = u / (NG * DB), db = (u / NG) % DB, g = u % NG;
           oacc[g][db] = mfma32(join_tr(vlo[ks][db], vhi[ks][db]), pp[g][ks], oacc[g][db]);
         }
         // VALU work on P(j)
 #pragma unroll
-        for (int v = 0; v < 32; ++v) {
+        for (int v = 0; v < NV; ++v) {
           const int g = v / 16, i = v % 16;
           if ((fma_slot(v) < -1 ? -1 : fma_slot(v)) == t) c[g][i] = __builtin_fmaf(c[g][i], c2, mneg[g]);
           if (exp_slot(v) == t) c[g][i] = exp2_fast(c[g][i]);
           if (add_slot(v) == t) acc[g][i % 4] = i < 4 ? c[g][i] : acc[g][i % 4] + c[g][i];
         }
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
+        for (int q = 0; q < NV / 2; ++q) {
           const int g = q / 8, i = 2 * (q % 8);
           if (cvt_slot(q) == t) {
             pr[q] = cvt_bf16x2(c[g][i], c[g][i + 1]);
@@ -587,7 +608,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
         }
         // rounded sums of P(j-1) on the matrix core (one 16x16x32 MFMA per k-step and group)
 #pragma unroll
-        for (int k = 0; k < 2 * KS; ++k)
+        for (int k = 0; k < NG * KS; ++k)
           if (lsum_slot(k) == t) lsum[k / KS] = mfma16(sel, pp[k / KS][k % KS], lsum[k / KS]);
         __builtin_amdgcn_sched_barrier(0);
       };
@@ -600,11 +621,11 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
       __builtin_amdgcn_sched_barrier(0);
       static_for<0, NSLOT + 1>(slot);
       // tail: this lane's sums of P(j), the bf16 operands of P(j)
-      float bs[2];
+      float bs[NG];
 #pragma unroll
-      for (int g = 0; g < 2; ++g) bs[g] = (acc[g][0] + acc[g][1]) + (acc[g][2] + acc[g][3]);
+      for (int g = 0; g < NG; ++g) bs[g] = (acc[g][0] + acc[g][1]) + (acc[g][2] + acc[g][3]);
 #pragma unroll
-      for (int g = 0; g < 2; ++g)
+      for (int g = 0; g < NG; ++g)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const int q = 8 * g + 4 * ks;
@@ -612,23 +633,27 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
                                               __builtin_shufflevector(pr[q + 2], pr[q + 3], 0, 1, 2, 3),
                                               0, 1, 2, 3, 4, 5, 6, 7);
         }
-      pin(pc[0], bs[0]);
-      asm volatile("" : "+v"(lsum[0]), "+v"(lsum[1]));
-      pin(pc[1], bs[1]);
+      bool big = false;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        pin(pc[g], bs[g]);
+        asm volatile("" : "+v"(lsum[g]));
+        big = big || bs[g] > kPMax;
+      }
       __builtin_amdgcn_sched_barrier(0);
       // (the rescale of O sits in a branch of its own: inside the rescue branch it made the
       // register allocator move output accumulators through AGPRs on every step)
-      const bool over = wave_any(bs[0] > kPMax || bs[1] > kPMax);
-      float alpha[2];
+      const bool over = wave_any(big);
+      float alpha[NG];
       if (over) rescue(kb0 + j * kBC, pc, bs, alpha);
       // a diagonal or ragged block is masked only now
       if (j + 1 < wtiles && edge(kb0 + (j + 1) * kBC)) mask(n, kb0 + (j + 1) * kBC);
       if (over) {
-        rescale(0, alpha[0]);
-        rescale(1, alpha[1]);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) rescale(g, alpha[g]);
       }
-      l_part[0] += bs[0];
-      l_part[1] += bs[1];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) l_part[g] += bs[g];
       __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of K(j+2), V(j) have landed
       __syncthreads();
     };
@@ -645,18 +670,21 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
     auto pre_step = [&](auto phase, int j) {
       constexpr int PH = decltype(phase)::value;
       constexpr bool ODD = PH & 1;
-      f32x16(&n)[2] = ODD ? sA : sB;       // S(j+1), where step j+1 reads it
-      bf16x8(&pz)[2][KS] = ODD ? pB : pA;  // P(j), step j+1's previous block
+      f32x16(&n)[NG] = ODD ? sA : sB;       // S(j+1), where step j+1 reads it
+      bf16x8(&pz)[NG][KS] = ODD ? pB : pA;  // P(j), step j+1's previous block
       issue(KT(), std::integral_constant<int, PH>(), min(j + 2, ntiles - 1));
       issue(VT(), std::integral_constant<int, PH>(), j);
 #pragma unroll
-      for (int g = 0; g < 2; ++g)
+      for (int g = 0; g < NG; ++g)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) pz[g][ks] = bf16x8{};
       qk(n, std::integral_constant<int, PH + 1>());
-      asm volatile("" : "+v"(n[0]), "+v"(n[1]));
+#pragma unroll
+      for (int g = 0; g < NG; ++g) asm volatile("" : "+v"(n[g]));
       if (edge(kb0 + (j + 1) * kBC)) mask(n, kb0 + (j + 1) * kBC);
-      const float mt[2] = {rowmax(n[0]), rowmax(n[1])};
+      float mt[NG];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) mt[g] = rowmax(n[g]);
       repivot(mt, pz);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -714,7 +742,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
     // the output is an exact convex combination of the rounded weights; the LSE uses the
     // unrounded sum.
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < NG; ++g) {
       const int myq = qw + 32 * g + r;
       const float l_tot = pair_sum(l_part[g]);
       // lane r's query sum sits in lsum of lane r (r < 16) or lane r + 16 (r >= 16)
