@@ -66,7 +66,8 @@ typedef enum {
   FA_ERR_DTYPE = -4,     /* dtype not supported by this entry point */
   FA_ERR_WORKSPACE = -5, /* workspace missing or smaller than the size query returned */
   FA_ERR_ARG = -6,       /* other invalid argument (scale, num_splits, flags) */
-  FA_ERR_HIP = -7        /* the HIP runtime reported an error launching a kernel */
+  FA_ERR_HIP = -7,       /* the HIP runtime reported an error launching a kernel */
+  FA_ERR_SCRATCH = -8    /* too large for the fixed scratch of fa_decode_noalloc */
 } fa_status;
 
 typedef enum { FA_DTYPE_F32 = 0, FA_DTYPE_BF16 = 1 } fa_dtype;
@@ -220,6 +221,27 @@ size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits);
 int fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
               int B, int H, int Hkv, int L, int d, float scale, int num_splits, int dtype,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_decode_noalloc — fa_decode for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, arguments, layouts and results as fa_decode,
+ * without the workspace arguments. The chunk partials go to a fixed 64 MiB
+ * scratch array inside the library instead: one per GPU, held from the first
+ * call on that GPU until the process ends. The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine); its first call on a device
+ * looks the array's address up once (hipGetSymbolAddress) and caches it.
+ *   Limit   B * H * num_splits * (d + 2) * 4 bytes (fa_decode_workspace_bytes)
+ *           must be at most 64 MiB, else FA_ERR_SCRATCH: e.g. B = 64, H = 32,
+ *           d = 128 takes up to 63 splits.
+ *   Sharing every call on one GPU uses the same array and leaves the last call's
+ *           partials in it (no call needs it cleared: every partial is written
+ *           before it is read). Calls that overlap on one GPU (other streams,
+ *           other host threads) race on it: serialise them.
+ */
+int fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                      int B, int H, int Hkv, int L, int d, float scale, int num_splits, int dtype,
+                      void* stream);
 
 /*
  * fa_decode_paged — fa_decode over a paged KV cache ("FlashAttention-2 and -3",

@@ -26,7 +26,7 @@ from ._clib import (  # noqa: F401
     FAError, FA_DTYPE_BF16, FA_DTYPE_F32, check, lib, strerror,
 )
 
-__all__ = ["fwd", "fwd_window", "fwd_fp8", "fwd_varlen", "bwd", "decode", "decode_paged", "FAError", "lib"]
+__all__ = ["fwd", "fwd_window", "fwd_fp8", "fwd_varlen", "bwd", "decode", "decode_noalloc", "decode_paged", "FAError", "lib"]
 
 
 def _torch():
@@ -234,6 +234,30 @@ def decode(q, k_cache, v_cache, scale=None, num_splits=64, workspace=None, out=N
                          B, H, Hkv, L, d, _scale(scale, d), num_splits, _dtype_code(q),
                          workspace.data_ptr(), workspace.numel(), _stream(q.device))
     check(st, "fa_decode")
+    return o, lse
+
+
+def decode_noalloc(q, k_cache, v_cache, out, scale=None, num_splits=64):
+    """decode() without a workspace and without allocating: the chunk partials go to the
+    library's fixed scratch (fa_decode_noalloc). `out` = (o [B, H, d] like q, lse fp32
+    [B, H]) is required. Calls that overlap on one GPU race on the scratch."""
+    torch = _torch()
+    _require((q, k_cache, v_cache), ("q", "k_cache", "v_cache"))
+    B, H, d = q.shape
+    if k_cache.dim() != 4:
+        raise ValueError("caches must be [B, L, Hkv, d]")
+    L, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape != (B, L, Hkv, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [B, L, Hkv, d] matching q")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share a dtype")
+    o, lse = out
+    _require((o, lse), ("o", "lse"))
+    if o.shape != q.shape or o.dtype != q.dtype or lse.shape != (B, H) or lse.dtype != torch.float32:
+        raise ValueError("out must be (o [B, H, d] like q, lse fp32 [B, H])")
+    st = lib().fa_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                 B, H, Hkv, L, d, _scale(scale, d), num_splits, _dtype_code(q), _stream(q.device))
+    check(st, "fa_decode_noalloc")
     return o, lse
 
 

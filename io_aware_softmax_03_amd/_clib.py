@@ -11,7 +11,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM = 0, -1, -2, -3
-FA_ERR_DTYPE, FA_ERR_WORKSPACE, FA_ERR_ARG, FA_ERR_HIP = -4, -5, -6, -7
+FA_ERR_DTYPE, FA_ERR_WORKSPACE, FA_ERR_ARG, FA_ERR_HIP, FA_ERR_SCRATCH = -4, -5, -6, -7, -8
 FA_DTYPE_F32, FA_DTYPE_BF16 = 0, 1
 
 # every symbol include/fa.h declares, with (restype, argtypes)
@@ -27,6 +27,7 @@ SIGNATURES = {
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
     "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
+    "fa_decode_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
     "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
 }
 

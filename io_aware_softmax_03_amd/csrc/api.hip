@@ -86,6 +86,8 @@ const char* fa_strerror(int status) {
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
     case FA_ERR_ARG: return "invalid argument (scale, flag, split count or pointer alignment)";
     case FA_ERR_HIP: return "HIP runtime error while launching a kernel";
+    case FA_ERR_SCRATCH:
+      return "problem too large for the fixed scratch of the allocation-free entry point (64 MiB)";
     default: return "unknown status";
   }
 }
@@ -207,6 +209,29 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, 
   if (!workspace || workspace_bytes < fa_decode_workspace_bytes(B, H, d, num_splits)) return FA_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace)) return FA_ERR_ARG;
   fa::DecodeArgs a{q, k_cache, v_cache, o, lse, (float*)workspace, B, H, Hkv, L, d, num_splits, scale,
+                   nullptr, nullptr, 0, 0, 0};
+  return from_hip(fa::launch_decode_bf16(a, (hipStream_t)stream));
+}
+
+int fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B,
+                      int H, int Hkv, int L, int d, float scale, int num_splits, int dtype, void* stream) {
+  if (B < 0 || L <= 0 || !heads_ok(H, Hkv)) return FA_ERR_SHAPE;
+  if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (!scale_ok(scale) || num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_ARG;
+  if (!fits(B, L, H, d)) return FA_ERR_SHAPE;
+  // the partials (fa_decode_workspace_bytes) must fit the fixed scratch; fits() bounds the
+  // product first so the comparison cannot overflow
+  if (!fits(B, H, num_splits, d + 2) ||
+      (long long)B * H * num_splits * (d + 2) * (long long)sizeof(float) > (long long)fa::kDecodeScratchBytes)
+    return FA_ERR_SCRATCH;
+  if (B == 0) return FA_OK;
+  if (!q || !k_cache || !v_cache || !o) return FA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return FA_ERR_ARG;
+  void* scratch = nullptr;
+  const hipError_t e = fa::decode_scratch(&scratch);
+  if (e != hipSuccess) return FA_ERR_HIP;
+  fa::DecodeArgs a{q, k_cache, v_cache, o, lse, (float*)scratch, B, H, Hkv, L, d, num_splits, scale,
                    nullptr, nullptr, 0, 0, 0};
   return from_hip(fa::launch_decode_bf16(a, (hipStream_t)stream));
 }

@@ -30,6 +30,8 @@
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
+#include <mutex>
+
 namespace fa {
 namespace {
 
@@ -508,6 +510,39 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Scratch of fa_decode_noalloc, for callers that cannot allocate device memory: the chunk
+// partials (running max, sum and d-wide output per (batch, head, split), the fa_decode
+// workspace layout) live in this fixed array instead of a caller workspace. Each GPU the
+// library runs on holds its own copy until the process ends. Every partial is written by
+// its split kernel before the combine kernel reads it, so nothing needs clearing between
+// calls; calls that overlap on one GPU share the array and race.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// Device address of `scratch` on the current device. The host-side name of the array is
+// only a handle for the symbol lookup; kernels get this address.
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
   if (a.head_dim == 128) return launch_t<128>(a, stream);

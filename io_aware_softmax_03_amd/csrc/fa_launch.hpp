@@ -69,6 +69,11 @@ struct DecodeArgs {
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 
+// Fixed device scratch of the allocation-free decode (fa_decode_noalloc): bytes, and its
+// address on the current device (looked up once per device, then cached).
+constexpr size_t kDecodeScratchBytes = size_t(64) << 20;
+hipError_t decode_scratch(void** ptr);
+
 // FP8 forward: bf16 Q, K, V are quantized into the workspace, then attended in e4m3.
 struct Fp8Args {
   const void* q;       // bf16 [B, N, H, d]

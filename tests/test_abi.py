@@ -41,7 +41,7 @@ def test_status_codes_match_header():
 
 def test_strerror():
     lib = _clib.lib()
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         assert lib.fa_strerror(code)
     assert b"unknown" in lib.fa_strerror(42)
 
@@ -162,6 +162,36 @@ def decode(**kw):
 ])
 def test_decode_rejects(kw, code):
     assert decode(**kw) == code
+
+
+def decode_noalloc(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, lse=None, B=2, H=4, Hkv=4, L=1000, d=128, scale=0.1, splits=8,
+             dtype=_clib.FA_DTYPE_BF16, stream=None)
+    a.update(kw)
+    return _clib.lib().fa_decode_noalloc(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(splits=0), _clib.FA_ERR_ARG), (dict(splits=1025), _clib.FA_ERR_ARG), (dict(L=0), _clib.FA_ERR_SHAPE),
+    (dict(dtype=_clib.FA_DTYPE_F32), _clib.FA_ERR_DTYPE), (dict(kc=None), _clib.FA_ERR_NULL),
+    (dict(d=100), _clib.FA_ERR_HEADDIM), (dict(q=FAKE + 8), _clib.FA_ERR_ARG), (dict(Hkv=3), _clib.FA_ERR_SHAPE),
+    # partials above the 64 MiB scratch: 64 * 32 * 64 * 130 * 4 bytes = 65 MiB
+    (dict(B=64, H=32, Hkv=32, L=32768, splits=64), _clib.FA_ERR_SCRATCH),
+    (dict(B=1 << 20, H=1 << 10, Hkv=1 << 10, L=1, splits=1024), _clib.FA_ERR_SCRATCH),
+])
+def test_decode_noalloc_rejects(kw, code):
+    assert decode_noalloc(**kw) == code
+
+
+def test_decode_noalloc_limit_is_64_mib():
+    # 64 * 32 * 63 * 130 * 4 bytes fit the scratch; the same call with 64 splits does not
+    assert 64 * 32 * 63 * 130 * 4 <= 64 << 20 < 64 * 32 * 64 * 130 * 4
+    assert decode_noalloc(B=64, H=32, Hkv=32, L=32768, splits=64, q=None) == _clib.FA_ERR_SCRATCH
+    assert decode_noalloc(B=64, H=32, Hkv=32, L=32768, splits=63, q=None) == _clib.FA_ERR_NULL
+
+
+def test_decode_noalloc_empty_batch_is_a_no_op():
+    assert decode_noalloc(B=0, q=None, kc=None, vc=None, o=None) == _clib.FA_OK
 
 
 def decode_paged(**kw):
