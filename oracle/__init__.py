@@ -31,7 +31,7 @@ from .attention import (  # noqa: F401
     attn_decode, attn_decode_slice, attn_decode_paged,
 )
 from .fp8 import (  # noqa: F401
-    round_e4m3, hadamard, rotation, fwht_f32, rotate_unnormalised, scale_exponent, block_exponents, quantize_rows, fp8_online_attention, fp8_operands, kernel_score_scale_log2,
+    round_e4m3, hadamard, rotation, fwht_f32, rotate_unnormalised, scale_exponent, block_exponents, quantize_rows, fp8_online_attention, fp8_operands, fp8_p_operand,
     fp8_attention_head,
     attn_fwd_fp8,
 )

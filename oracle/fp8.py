@@ -29,12 +29,9 @@ Readings where the page is silent (each listed in the design notes):
   Q, K and V alike.
 * P is quantized per key block as the online algorithm forms it: P~ = exp(S - m_new) in
   (0, 1] against the running maximum, times 2^8, rounded to e4m3, divided by 2^8. The row
-  sum l and the LSE use the unquantized P~; O~ accumulates the quantized P times V.
-* The code of P~ is again an integer the float arithmetic decides. With
-  `score_scale_log2` given, the exponent is formed as the kernel forms it: the score S in
-  float32, times that float32 factor (scale * log2 e, over d after a rotation), minus the
-  running maximum of those values, in float32; then 2 to that power (in float64: the
-  hardware's 2^x is within an ulp of it).
+  sum l and the LSE use the unquantized P~; O~ accumulates the quantized P times V. The
+  scores, maxima and exponentials are float64 here; a kernel forming them in float32 can
+  take the neighbouring code for a P~ * 2^8 within float32 rounding of a rounding midpoint.
 """
 from __future__ import annotations
 
@@ -133,57 +130,39 @@ def quantize_rows(x, block_rows: int):
     return round_e4m3(x / scale[:, None]) * scale[:, None], e
 
 
-def fp8_online_attention(q, k, v, scale, causal=False, block_cols=64, quantize_p=True, row_offset=0,
-                         score_scale_log2=None):
-    """The tiled online softmax on (already quantized) operands, q [Nq, d], k, v [Nk, d]:
-    per key block of `block_cols` (counted from key 0), P~ = exp(S - m_new) against the
-    running maximum, quantized as e4m3(P~ * 2^8) / 2^8 for the second product; the row sum
-    and the LSE use P~ itself. Query row i sits at position row_offset + i (causal: it sees
-    keys up to that position). With `score_scale_log2` (a float32 factor), scores and
-    maxima are kept in base 2 and float32 as the kernel keeps them (module notes); `scale`
-    is then unused. Returns (O, LSE)."""
+def fp8_p_operand(P) -> np.ndarray:
+    """The P operand of the second product: e4m3(P * 2^8) / 2^8 (module notes)."""
+    return round_e4m3(np.asarray(P, dtype=np.float64) * 2.0 ** P_SCALE_LOG2) * 2.0 ** -P_SCALE_LOG2
+
+
+def fp8_online_attention(q, k, v, scale, causal=False, block_cols=64, quantize_p=True, row_offset=0):
+    """The tiled online softmax on (already quantized) operands, q [Nq, d], k, v [Nk, d],
+    in float64: per key block of `block_cols` (counted from key 0), P~ = exp(S - m_new)
+    against the running maximum, quantized as e4m3(P~ * 2^8) / 2^8 for the second product;
+    the row sum and the LSE use P~ itself. Query row i sits at position row_offset + i
+    (causal: it sees keys up to that position). Returns (O, LSE)."""
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     nq, nk = q.shape[0], k.shape[0]
-    f32 = score_scale_log2 is not None
-    m = np.full(nq, -np.inf, dtype=np.float32 if f32 else np.float64)
+    m = np.full(nq, -np.inf)
     l = np.zeros(nq)
     acc = np.zeros((nq, v.shape[1]))
     rows = row_offset + np.arange(nq)[:, None]
     for j0 in range(0, nk, block_cols):
         j1 = min(j0 + block_cols, nk)
-        if f32:
-            S = (q @ k[j0:j1].T).astype(np.float32) * np.float32(score_scale_log2)
-        else:
-            S = float(scale) * (q @ k[j0:j1].T)
+        S = float(scale) * (q @ k[j0:j1].T)
         if causal:
-            S = np.where(np.arange(j0, j1)[None, :] <= rows, S, -np.inf).astype(S.dtype)
+            S = np.where(np.arange(j0, j1)[None, :] <= rows, S, -np.inf)
         m_new = np.maximum(m, S.max(axis=1))
-        m_ref = np.where(np.isfinite(m_new), m_new, 0.0).astype(m_new.dtype)
-        if f32:
-            alpha = np.where(np.isfinite(m), np.exp2((m - m_ref).astype(np.float64)), 0.0)
-            P = np.exp2((S - m_ref[:, None]).astype(np.float64))
-        else:
-            alpha = np.where(np.isfinite(m), np.exp(m - m_ref), 0.0)
-            P = np.exp(S - m_ref[:, None])
-        Pq = round_e4m3(P * 2.0 ** P_SCALE_LOG2) * 2.0 ** -P_SCALE_LOG2 if quantize_p else P
+        m_ref = np.where(np.isfinite(m_new), m_new, 0.0)
+        alpha = np.where(np.isfinite(m), np.exp(m - m_ref), 0.0)
+        P = np.exp(S - m_ref[:, None])
+        Pq = fp8_p_operand(P) if quantize_p else P
         l = alpha * l + P.sum(axis=1)
         acc = alpha[:, None] * acc + Pq @ v[j0:j1]
         m = m_new
     O = acc / np.where(l > 0, l, 1.0)[:, None]
-    m = m.astype(np.float64)
-    if f32:
-        lse = np.where(l > 0, (np.where(np.isfinite(m), m, 0.0) + np.log2(np.where(l > 0, l, 1.0))) * math.log(2.0),
-                       -np.inf)
-    else:
-        lse = np.where(l > 0, np.where(np.isfinite(m), m, 0.0) + np.log(np.where(l > 0, l, 1.0)), -np.inf)
+    lse = np.where(l > 0, np.where(np.isfinite(m), m, 0.0) + np.log(np.where(l > 0, l, 1.0)), -np.inf)
     return O, lse
-
-
-def kernel_score_scale_log2(scale, d, rotated):
-    """The float32 factor the kernel puts on the scores: scale * log2(e) in float32, divided
-    by d after a rotation."""
-    c = np.float32(np.float32(scale) * np.float32(1.4426950408889634))
-    return np.float32(c / np.float32(d)) if rotated else c
 
 
 def fp8_operands(q, k, v, scale, signs=None, block_rows=64, quantize=True):
@@ -204,7 +183,7 @@ def fp8_operands(q, k, v, scale, signs=None, block_rows=64, quantize=True):
 
 
 def fp8_attention_head(q, k, v, scale, causal=False, signs=None, block_rows=64, block_cols=64,
-                       quantize=True, kernel_precision=False):
+                       quantize=True):
     """FP8 forward for one (batch, head) slice, q [Nq, d], k, v [Nk, d]; returns (O, LSE).
 
     Steps: rotate q and k by R (when `signs` is given), block-quantize q, k and v, then the
@@ -212,12 +191,10 @@ def fp8_attention_head(q, k, v, scale, causal=False, signs=None, block_rows=64, 
     ``quantize=False`` skips both quantizations (the same algorithm in float64), and
     block_rows >= the length gives one scale per tensor slice."""
     qh, kh, vh, sc = fp8_operands(q, k, v, scale, signs, block_rows, quantize)
-    c2 = kernel_score_scale_log2(scale, q.shape[1], signs is not None) if kernel_precision else None
-    return fp8_online_attention(qh, kh, vh, sc, causal, block_cols, quantize, score_scale_log2=c2)
+    return fp8_online_attention(qh, kh, vh, sc, causal, block_cols, quantize)
 
 
-def attn_fwd_fp8(q, k, v, scale, causal=False, signs=None, block_rows=64, block_cols=64, quantize=True,
-                 kernel_precision=False):
+def attn_fwd_fp8(q, k, v, scale, causal=False, signs=None, block_rows=64, block_cols=64, quantize=True):
     """Dense FP8 forward. q: [B, N, H, d]; k, v: [B, N, Hkv, d] (grouped as in attn_fwd).
     Returns O [B, N, H, d], LSE [B, H, N]."""
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
@@ -229,5 +206,5 @@ def attn_fwd_fp8(q, k, v, scale, causal=False, signs=None, block_rows=64, block_
         for h in range(H):
             j = h // (H // Hkv)
             O[b, :, h], lse[b, h] = fp8_attention_head(q[b, :, h], k[b, :, j], v[b, :, j], scale, causal, signs,
-                                                       block_rows, block_cols, quantize, kernel_precision)
+                                                       block_rows, block_cols, quantize)
     return O, lse

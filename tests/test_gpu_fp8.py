@@ -1,18 +1,29 @@
-"""GPU parity of fa_fwd_fp8 against the FP8 emulation in the oracle, and the page's
-accuracy claim against exact float64 attention.
+"""GPU parity of fa_fwd_fp8 against the FP8 emulation in the oracle (float64), and the
+page's accuracy claim against exact float64 attention ("FlashAttention-2 and -3", "FP8, and
+the outlier problem").
 
 Quantization is integer work and is checked bit for bit: the e4m3 codes of Q, K (rotated)
 and V and every block exponent, read back from the workspace, equal the oracle's.
 
-The attention stage is floating point. The emulation forms the exponents of P as the kernel
-does (float32 scores times the kernel's float32 factor, minus the running maximum), but the
-FP8 matrix core accumulates the score products in its own order and precision (the LSE
-shows scores a few 1e-6 relative apart), so P * 2^8 near an e4m3 rounding midpoint can take
-the neighbouring code. A code moves its weight by at most one e4m3 step, 2^-3 of it, so for
-every output element |O - O_emulated| <= 2^-3 sum_j (p_j / l) |v_j| + 2^-8 |O| + 2e-3 (the
-last two terms: bf16 rounding of O, fp32 sums). Flips on large weights are rare, so at most
-5% of the rows may leave the tight bound 2^-8 |O| + 2e-3; a wrong key order, scale or layout
-moves nearly every row. LSE: within 1e-3 (unquantized sums on both sides)."""
+The attention stage is floating point. The emulation forms every P = exp(S - m) in float64,
+the kernel in float32 (its scores come from the FP8 matrix core's float32 accumulation, its
+exponent from a float32 scale factor). The FP8 matrix core sums the products of a score
+more coarsely than float32: measured on the outlier inputs, the kernel's scores (seen
+through its LSE) sit up to 2.8e-5 (about 2^-15) of A = scale * sum_i |q_i k_i| away from
+the float64 ones. Taking TAU = 2^-13 (four times that), P_j's relative error is at most
+TAU (A_j + A_max), A_max the row's largest A (the running maximum's own error). A weight
+can then take the neighbouring e4m3 code only if P * 2^8 lies within that relative
+distance of a rounding midpoint (call it ambiguous); its weight then moves by one e4m3 step
+(the spacing at that magnitude, over 2^8). The unquantized row sum and the block rescaling
+move by the same relative error. So for every output element
+
+  |O - O_emulated| <= sum over ambiguous j of step_j * w_j * |v_j| / l
+                      + 4 TAU A_max sum_j (p_j / l) |v_j|
+                      + 2^-8 |O_emulated| + 2e-3,
+
+w_j rescaling weight j from its block's running maximum to the row's final one, p_j / l
+the softmax weights (the last two terms: bf16 rounding of O, float32 accumulation). The
+bound is applied to every element, with no exception. LSE: within 1e-3."""
 import math
 
 import numpy as np
@@ -62,21 +73,44 @@ def workspace_operands(ws, B, H, Hkv, N, d):
     return q8[:, :, :N] * sc[0], k8[:, :, :N] * sc[1], v8[:, :, :N] * sc[2], ex
 
 
-def check_row_bounds(o, o_ref, p_over_l, vabs):
-    """o, o_ref [rows, d]; p_over_l [rows, keys]; vabs [keys, d]."""
-    err = np.abs(o - o_ref)
-    loose = 2.0 ** -3 * (p_over_l @ vabs) + 2.0 ** -8 * np.abs(o_ref) + 2e-3
-    assert np.all(err <= loose), float((err - loose).max())
-    return np.any(err > 2.0 ** -8 * np.abs(o_ref) + 2e-3, axis=1)
+TAU = 2.0 ** -13  # score error of the FP8 matrix core, relative to scale * sum_i |q_i k_i| (notes)
 
 
-def weights(qh, kh, sc, causal, row0=0):
-    """Softmax weights p_j / l (float64, unquantized) of rows row0.. of one head."""
+def code_slack(qh, kh, vh, sc, causal, row0=0, block_cols=64):
+    """Per-element bound [rows, d] on |O - O_emulated| beyond the output rounding (module
+    notes), for query rows row0.. of one head (operands already quantized, as the emulation
+    takes them). Returns (bound, number of ambiguous P codes)."""
+    nq, nk = qh.shape[0], kh.shape[0]
     S = sc * (qh @ kh.T)
+    A = abs(sc) * (np.abs(qh) @ np.abs(kh).T)  # the magnitude each score's products sum from
     if causal:
-        S = np.where(np.arange(kh.shape[0])[None, :] <= row0 + np.arange(qh.shape[0])[:, None], S, -np.inf)
-    P = np.exp(S - S.max(axis=1, keepdims=True))
-    return P / P.sum(axis=1, keepdims=True)
+        vis = np.arange(nk)[None, :] <= row0 + np.arange(nq)[:, None]
+        S = np.where(vis, S, -np.inf)
+        A = np.where(vis, A, 0.0)
+    a_max = A.max(axis=1, keepdims=True)
+    nb = -(-nk // block_cols)
+    bmax = np.stack([S[:, b * block_cols:(b + 1) * block_cols].max(axis=1) for b in range(nb)], axis=1)
+    run = np.maximum.accumulate(bmax, axis=1)           # running maximum after each block
+    m_blk = np.repeat(run, block_cols, axis=1)[:, :nk]  # the maximum P of key j is formed against
+    m_fin = run[:, -1:]
+    x = np.exp(S - m_blk) * 2.0 ** 8
+    e = np.clip(np.floor(np.log2(np.where(x > 0, x, 1.0))), -6, 8)
+    sp = np.exp2(e - 3)                                  # e4m3 spacing at x
+    dist = np.abs(x / sp - np.floor(x / sp) - 0.5) * sp  # distance to the nearest rounding midpoint
+    amb = (x > 0) & (dist <= TAU * (A + a_max) * x)      # P's relative error reaches the midpoint
+    p = np.exp(S - m_fin)
+    l = p.sum(axis=1, keepdims=True)
+    flips = np.where(amb, sp * 2.0 ** -8 * np.exp(m_blk - m_fin), 0.0) / l
+    # codes that can flip, plus the unquantized sum and the rescaling moving by the same
+    # relative score error
+    return flips @ np.abs(vh) + 4 * TAU * a_max * ((p / l) @ np.abs(vh)), int(amb.sum())
+
+
+def check_elements(o, o_ref, slack):
+    err = np.abs(o - o_ref)
+    bound = slack + 2.0 ** -8 * np.abs(o_ref) + 2e-3
+    assert np.all(err <= bound), float((err - bound).max())
+    return float((err / bound).max())
 
 
 @pytest.mark.parametrize("B,N,H,Hkv,d,causal,rotate", [
@@ -99,8 +133,7 @@ def test_fwd_fp8_matches_emulation(B, N, H, Hkv, d, causal, rotate):
     o, lse = host(o), host(lse)
     qg, kg, vg, _ = workspace_operands(ws.cpu().numpy(), B, H, Hkv, N, d)
     qf, kf, vf = bits_to_f64(q), bits_to_f64(k), bits_to_f64(v)
-    c2 = oracle.kernel_score_scale_log2(1 / math.sqrt(d), d, rotate)
-    loose_rows = total_rows = 0
+    worst, ambiguous = 0.0, 0
     for b in range(B):
         for h in range(H):
             j = h // (H // Hkv)
@@ -109,13 +142,12 @@ def test_fwd_fp8_matches_emulation(B, N, H, Hkv, d, causal, rotate):
             np.testing.assert_array_equal(qg[b, h], qh)
             np.testing.assert_array_equal(kg[b, j], kh)
             np.testing.assert_array_equal(vg[b, j], vh)
-            o_ref, lse_ref = oracle.fp8_online_attention(qh, kh, vh, sc, causal, score_scale_log2=c2)
+            o_ref, lse_ref = oracle.fp8_online_attention(qh, kh, vh, sc, causal)
             assert np.max(np.abs(lse[b, h] - lse_ref)) <= 1e-3
-            out = check_row_bounds(o[b, :, h], o_ref, weights(qh, kh, sc, causal), np.abs(vh))
-            loose_rows += int(out.sum())
-            total_rows += N
-    print(f"fp8 parity: rows outside the tight bound {loose_rows} of {total_rows}")
-    assert loose_rows <= 0.05 * total_rows
+            slack, n_amb = code_slack(qh, kh, vh, sc, causal)
+            worst = max(worst, check_elements(o[b, :, h], o_ref, slack))
+            ambiguous += n_amb
+    print(f"fp8 parity: largest error / bound {worst:.3f}; ambiguous P codes {ambiguous}")
 
 
 def test_fwd_fp8_outlier_accuracy():
@@ -147,18 +179,14 @@ def test_fwd_fp8_full_size_sampled_rows():
     o, lse = fa().fwd_fp8(q, k, v, signs=dev_f32(signs), causal=True)
     o, lse = host(o), host(lse)
     rng = np.random.default_rng(3)
-    c2 = oracle.kernel_score_scale_log2(1 / math.sqrt(d), d, True)
-    loose = total = 0
+    worst = 0.0
     for b, h in ((0, 0), (1, 9)):
         qh, kh, vh, sc = oracle.fp8_operands(host(q[b, :, h]), host(k[b, :, h]), host(v[b, :, h]), 1 / math.sqrt(d),
                                              signs)
         for i in sorted(set([0, 63, 64, 4095, N - 1] + list(rng.integers(0, N, 4)))):
-            o_ref, lse_ref = oracle.fp8_online_attention(qh[i:i + 1], kh[:i + 1], vh[:i + 1], sc, True, row_offset=i,
-                                                         score_scale_log2=c2)
-            out = check_row_bounds(o[b, i:i + 1, h], o_ref, weights(qh[i:i + 1], kh[:i + 1], sc, True, i),
-                                   np.abs(vh[:i + 1]))
-            loose += int(out.sum())
-            total += 1
+            o_ref, lse_ref = oracle.fp8_online_attention(qh[i:i + 1], kh[:i + 1], vh[:i + 1], sc, True, row_offset=i)
+            slack, _ = code_slack(qh[i:i + 1], kh[:i + 1], vh[:i + 1], sc, True, row0=i)
+            worst = max(worst, check_elements(o[b, i:i + 1, h], o_ref, slack))
             assert abs(lse[b, h, i] - lse_ref[0]) <= 1e-3, (b, h, i)
-    assert loose <= max(1, 0.1 * total)
+    print(f"fp8 full size: largest error / bound {worst:.3f}")
     assert np.isfinite(o).all() and np.isfinite(lse).all()

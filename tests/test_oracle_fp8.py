@@ -11,7 +11,10 @@
 * The page's outlier test (entries N(0,1) plus N(0,100) on 0.1% of them, d = 128): rotation
   cuts the RMSE against float64 attention (the page: 9.1e-3 against 2.4e-2), and block
   against per-tensor scaling changes little (9.1e-3 against 9.3e-3).
-Planted mistakes (K not rotated, a scale exponent one too small) are checked to be caught."""
+* The P operand of the second product, e4m3(P * 2^8) / 2^8 formed per key block against the
+  running maximum, on closed-form cases in the normal and the subnormal e4m3 range.
+Planted mistakes (K not rotated, a scale exponent one too small, P scaled by 2^7 or 2^9,
+P not quantized, P quantized against the final maximum) are checked to be caught."""
 import math
 
 import numpy as np
@@ -123,19 +126,70 @@ def test_unquantized_emulation_is_exact_attention(causal):
         np.testing.assert_allclose(got[1], ref[1], atol=tol)
 
 
-def test_kernel_precision_path_agrees_with_float64():
-    """The float32 base-2 formation of the exponents changes the result by float32 rounding
-    only (P unquantized), and with P quantized by at most a few flipped e4m3 codes."""
-    q, k, v = np.random.default_rng(4).standard_normal((3, 200, 64))
-    d = 64
-    ref = oracle.fp8_online_attention(q, k, v, 1 / 8, True, quantize_p=False)
-    c2 = oracle.kernel_score_scale_log2(1 / 8, d, False)
-    got = oracle.fp8_online_attention(q, k, v, 1 / 8, True, quantize_p=False, score_scale_log2=c2)
-    np.testing.assert_allclose(got[0], ref[0], atol=1e-5)
-    np.testing.assert_allclose(got[1], ref[1], atol=1e-5)
-    refq = oracle.fp8_online_attention(q, k, v, 1 / 8, True)
-    gotq = oracle.fp8_online_attention(q, k, v, 1 / 8, True, score_scale_log2=c2)
-    assert np.mean(np.abs(gotq[0] - refq[0]).max(axis=1) > 1e-5) < 0.05
+def _keys_case(scores, values, d=4):
+    """One query against keys with the given scores (scale 1, q = e_0) and values (v_j = value
+    in every dimension)."""
+    q = np.zeros((1, d))
+    q[0, 0] = 1.0
+    k = np.zeros((len(scores), d))
+    k[:, 0] = scores
+    v = np.repeat(np.asarray(values, dtype=np.float64)[:, None], d, axis=1)
+    return q, k, v
+
+
+def p_quantization_pins():
+    """Closed forms of the P operand e4m3(P * 2^8) / 2^8 (raises AssertionError on a mismatch).
+
+    1. Normal range: key 0 scores 0 (the maximum: P = 1, value 0), key 1 scores ln 0.3
+       (P = 0.3, value 1). 0.3 * 2^8 = 76.8 lies in [64, 128) where e4m3 values are 8 apart:
+       it rounds to 80, P~ = 0.3125, O = 0.3125 / 1.3; the LSE uses the unquantized sum:
+       ln 1.3.
+    2. Subnormal range: P = 1.3 * 2^-17, value 2^17. P * 2^8 = 1.3 * 2^-9, and below 2^-6
+       e4m3 values are 2^-9 apart: it rounds to 2^-9, P~ = 2^-17, O = 1 / (1 + P). (A 2^7
+       scale would give 2^-16 and O = 2 / (1 + P); no quantization 1.3 / (1 + P).)
+    3. Per block against the running maximum: blocks of two keys, scores 0, ln 0.3 | ln 3,
+       values 0, 1 | 0. Block 0 quantizes 0.3 -> 0.3125 against the maximum 0; block 1 moves
+       the maximum to ln 3 and rescales by 1/3: O = 0.3125 / 4.3. (Quantizing against the
+       final maximum would round 0.1 * 2^8 = 25.6 to 26 instead: O = 0.3046875 / 4.3.)"""
+    q, k, v = _keys_case([0.0, math.log(0.3)], [0.0, 1.0])
+    O, lse = oracle.fp8_online_attention(q, k, v, 1.0)
+    assert abs(O[0, 0] - 0.3125 / 1.3) <= 1e-14 and np.all(O[0] == O[0, 0])
+    assert abs(lse[0] - math.log(1.3)) <= 1e-14
+    p = 1.3 * 2.0 ** -17
+    q, k, v = _keys_case([0.0, math.log(p)], [0.0, 2.0 ** 17])
+    O, _ = oracle.fp8_online_attention(q, k, v, 1.0)
+    assert abs(O[0, 0] - 1.0 / (1.0 + p)) <= 1e-12
+    q, k, v = _keys_case([0.0, math.log(0.3), math.log(3.0)], [0.0, 1.0, 0.0])
+    O, lse = oracle.fp8_online_attention(q, k, v, 1.0, block_cols=2)
+    assert abs(O[0, 0] - 0.3125 / 4.3) <= 1e-14
+    assert abs(lse[0] - math.log(4.3)) <= 1e-14
+
+
+def test_p_quantization_closed_form():
+    p_quantization_pins()
+    # the operand itself on exact values: 1 stays 1; 2^-8 * (the e4m3 grid) is fixed
+    t = e4m3_table()
+    np.testing.assert_array_equal(oracle.fp8_p_operand(t * 2.0 ** -8), t * 2.0 ** -8)
+    assert oracle.fp8_p_operand(np.array([1.0]))[0] == 1.0
+
+
+@pytest.mark.parametrize("mistake", ["scale 2^7", "scale 2^9", "not quantized", "final maximum"])
+def test_p_quantization_mistakes_are_caught(monkeypatch, mistake):
+    if mistake == "scale 2^7":
+        monkeypatch.setattr(fp8, "P_SCALE_LOG2", 7)
+    elif mistake == "scale 2^9":
+        monkeypatch.setattr(fp8, "P_SCALE_LOG2", 9)
+    elif mistake == "not quantized":
+        monkeypatch.setattr(fp8, "fp8_p_operand", lambda P: np.asarray(P, dtype=np.float64))
+    else:
+        real = fp8.fp8_online_attention
+
+        def final_max(q, k, v, scale, causal=False, block_cols=64, quantize_p=True, row_offset=0):
+            # quantizes P against the row's final maximum (one block covering every key)
+            return real(q, k, v, scale, causal, max(block_cols, k.shape[0]), quantize_p, row_offset)
+        monkeypatch.setattr(oracle, "fp8_online_attention", final_max)
+    with pytest.raises(AssertionError):
+        p_quantization_pins()
 
 
 def outlier_rmse(**kw):
