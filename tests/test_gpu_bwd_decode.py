@@ -57,18 +57,21 @@ def test_bwd_small(B, N, H, d, causal):
     assert max_abs(dv, rv) <= TOL_GRAD
 
 
-def test_bwd_full_size_sampled_heads():
-    """Causal B=4, H=16, N=4096, d=128 as the bench runs it; three whole heads are checked
-    against the oracle, and the gradient-sum invariants are checked on every head."""
+def test_bwd_full_size_every_head():
+    """Causal B=4, H=16, N=4096, d=128 as the bench runs it: every element of dQ, dK and dV of
+    all 64 heads against the oracle, and the gradient-sum invariants on every head."""
     B, N, H, d = 4, 4096, 16, 128
     (qb, kb, vb, gb), (dq, dk, dv) = run_bwd(4, B, N, H, d, True)
     scale = 1 / math.sqrt(d)
-    for (b, h) in [(0, 0), (2, 9), (3, 15)]:
-        g = oracle.attn_bwd_head(bits_to_f64(qb[b, :, h]), bits_to_f64(kb[b, :, h]), bits_to_f64(vb[b, :, h]),
-                                 bits_to_f64(gb[b, :, h]), scale, True)
-        assert max_abs(dq[b, :, h], g["dq"]) <= TOL_GRAD, (b, h)
-        assert max_abs(dk[b, :, h], g["dk"]) <= TOL_GRAD, (b, h)
-        assert max_abs(dv[b, :, h], g["dv"]) <= TOL_GRAD, (b, h)
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            g = oracle.attn_bwd_head(bits_to_f64(qb[b, :, h]), bits_to_f64(kb[b, :, h]), bits_to_f64(vb[b, :, h]),
+                                     bits_to_f64(gb[b, :, h]), scale, True)
+            e = max(max_abs(dq[b, :, h], g["dq"]), max_abs(dk[b, :, h], g["dk"]), max_abs(dv[b, :, h], g["dv"]))
+            assert e <= TOL_GRAD, (b, h, e)
+            worst = max(worst, e)
+    print(f"full-size backward, all {B * H} heads: max gradient error {worst:.2e}")
     # rows of P sum to one: sum_j dV_j = sum_i dO_i; shift invariance: sum_j dK_j = 0
     do_sum = bits_to_f64(gb).sum(axis=1)
     assert max_abs(dv.sum(axis=1), do_sum) <= 0.5
@@ -121,9 +124,10 @@ def test_decode_split_invariance():
         assert max_abs(host(lse), host(outs[0][1])) <= 1e-5
 
 
-def test_decode_full_size_sampled_heads():
+def test_decode_full_size_batch_rows_and_samples():
     """B=64, H=32, L=32768, d=128 with 64 splits, as the bench runs it. The 34 GB of bf16
-    cache is drawn on the device; sampled (b, h) slices are copied back for the oracle."""
+    cache is drawn on the device; every head of batch rows 0 and 63 and sampled (b, h) slices
+    elsewhere are copied back for the oracle (all 2048 slices would copy the whole cache)."""
     torch = pytest.importorskip("torch")
     B, H, L, d = 64, 32, 32768, 128
     gen = torch.Generator(device="cuda")
@@ -134,7 +138,8 @@ def test_decode_full_size_sampled_heads():
     o, lse = fa().decode(q, kc, vc, num_splits=64)
     o, lse = host(o), host(lse)
     scale = 1 / math.sqrt(d)
-    for (b, h) in [(0, 0), (13, 5), (40, 31), (63, 17)]:
+    slices = [(b, h) for b in (0, 63) for h in range(H)] + [(13, 5), (40, 31), (27, 17), (51, 0)]
+    for (b, h) in slices:
         o_ref, lse_ref = oracle.attn_decode_slice(host(q[b, h]), host(kc[b, :, h]), host(vc[b, :, h]), scale)
         assert max_abs(o[b, h], o_ref) <= TOL_O, (b, h)
         assert abs(lse[b, h] - lse_ref) <= TOL_LSE, (b, h)
