@@ -121,11 +121,16 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* l
  *   lse          fp32 [H, total_tokens]
  *   cu_seqlens   device int32 [num_seqs + 1]: cu_seqlens[0] = 0, nondecreasing,
  *                cu_seqlens[num_seqs] = total_tokens. Sequence s occupies rows
- *                cu_seqlens[s] .. cu_seqlens[s+1]-1. The contents are the
- *                caller's contract (they live on the device and are not read by
- *                the host); rows of a sequence longer than max_seqlen are not
- *                written.
- *   max_seqlen   >= every sequence length; sizes the launch grid.
+ *                cu_seqlens[s] .. cu_seqlens[s+1]-1. The offsets live on the
+ *                device and the host does not read them (the Python binding
+ *                checks a host copy before the call). Offsets that break the
+ *                contract cannot make the kernels access memory outside the
+ *                tensors: sequence s is taken as rows max(0, min(c_s, T)) ..
+ *                min(max(c_{s+1}, that start), T) - 1 (T = total_tokens);
+ *                rows in no such range are not written.
+ *   max_seqlen   the longest sequence length; sizes the launch grid. A sequence
+ *                longer than max_seqlen is still computed in full (its extra
+ *                query blocks are taken by the same workgroups, more slowly).
  * Attention never crosses a sequence boundary (block-diagonal mask); causal is
  * counted within each sequence. Empty sequences are allowed.
  */

@@ -26,7 +26,7 @@ from ._clib import (  # noqa: F401
     FAError, FA_DTYPE_BF16, FA_DTYPE_F32, check, lib, strerror,
 )
 
-__all__ = ["fwd", "fwd_window", "fwd_fp8", "fwd_varlen", "bwd", "decode", "decode_noalloc", "decode_paged", "FAError", "lib"]
+__all__ = ["fwd", "fwd_window", "fwd_fp8", "fwd_varlen", "check_cu_seqlens", "bwd", "decode", "decode_noalloc", "decode_paged", "FAError", "lib"]
 
 
 def _torch():
@@ -148,19 +148,53 @@ def fwd_fp8(q, k, v, signs=None, scale=None, causal=False, out=None, workspace=N
     return o, lse
 
 
-def fwd_varlen(q, k, v, cu_seqlens, max_seqlen, scale=None, causal=False):
-    """Packed forward over sequences laid end to end. q: [T, H, d], k, v: [T, Hkv, d]; cu_seqlens: int32
-    device tensor [num_seqs + 1]; max_seqlen: the longest sequence length (host int).
+def check_cu_seqlens(cu, total_tokens, max_seqlen=None):
+    """Validate packed-sequence offsets on the host (a 1-D integer sequence or array):
+    cu[0] = 0, nondecreasing, cu[-1] = total_tokens, and no sequence longer than max_seqlen
+    (when given). Returns the longest sequence length; raises ValueError otherwise."""
+    import numpy as np
+    cu = np.asarray(cu, dtype=np.int64).reshape(-1)
+    if cu.size < 1 or cu[0] != 0:
+        raise ValueError("cu_seqlens must start with 0")
+    lengths = np.diff(cu)
+    if lengths.size and lengths.min() < 0:
+        raise ValueError("cu_seqlens must be nondecreasing")
+    if cu[-1] != total_tokens:
+        raise ValueError(f"cu_seqlens must end at total_tokens ({total_tokens}), got {int(cu[-1])}")
+    longest = int(lengths.max()) if lengths.size else 0
+    if max_seqlen is not None and longest > max_seqlen:
+        raise ValueError(f"a sequence of {longest} tokens exceeds max_seqlen = {max_seqlen}")
+    return longest
+
+
+def fwd_varlen(q, k, v, cu_seqlens, max_seqlen=None, scale=None, causal=False, validate=True):
+    """Packed forward over sequences laid end to end. q: [T, H, d], k, v: [T, Hkv, d];
+    cu_seqlens: int32 offsets [num_seqs + 1], a device tensor or host data (uploaded here);
+    max_seqlen: the longest sequence length (host int; computed from the offsets if None).
+    With validate (the default) the offsets are checked on the host first (check_cu_seqlens;
+    a device tensor is copied back for it, which waits for the stream). The kernels clamp the
+    offsets into the tensor and compute every row whatever max_seqlen says, so validate=False
+    is memory-safe; rows outside every [cu[s], cu[s+1]) range are then left unwritten.
     Returns O [T, H, d] and fp32 LSE [H, T]."""
     torch = _torch()
-    _require((q, k, v, cu_seqlens), ("q", "k", "v", "cu_seqlens"))
+    _require((q, k, v), ("q", "k", "v"))
     if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or k.shape[0] != q.shape[0] or k.shape[2] != q.shape[2]:
         raise ValueError("q must be [total_tokens, H, d] and k, v [total_tokens, Hkv, d]")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share a dtype")
-    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
-        raise TypeError("cu_seqlens must be a 1-D int32 tensor")
     T, H, d = q.shape
+    on_device = isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.is_cuda
+    if validate or max_seqlen is None:
+        host_cu = cu_seqlens.cpu() if isinstance(cu_seqlens, torch.Tensor) else cu_seqlens
+        longest = check_cu_seqlens(host_cu, T, max_seqlen)
+        if max_seqlen is None:
+            max_seqlen = max(longest, 1 if T > 0 else 0)
+    if on_device:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+            raise TypeError("cu_seqlens must be a 1-D int32 tensor")
+        _require((cu_seqlens,), ("cu_seqlens",))
+    else:
+        cu_seqlens = torch.as_tensor(cu_seqlens, dtype=torch.int32).reshape(-1).to(q.device)
     o = torch.empty_like(q)
     lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
     st = lib().fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),

@@ -169,8 +169,10 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
   }
   int seq_start, seq_start_k, L, Lk;  // L: query rows
   if constexpr (VARLEN) {
-    seq_start = p.cu_seqlens[bs];
-    L = p.cu_seqlens[bs + 1] - seq_start;
+    // offsets clamped into the packed tensor: a sequence starts in [0, T] and ends in
+    // [its start, T], so no access leaves the buffers whatever cu_seqlens holds
+    seq_start = min(max(p.cu_seqlens[bs], 0), p.total_rows);
+    L = min(max(p.cu_seqlens[bs + 1], seq_start), p.total_rows) - seq_start;
     seq_start_k = seq_start;
     Lk = L;
   } else {
@@ -771,12 +773,25 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) 
     }
   };
 
-  // (one inlined copy of the block body: the second pass reuses its registers)
-  const int heavy = CAUSAL ? nb - 1 - pi : pi;
-  const int passes = CAUSAL ? (pi < heavy ? 2 : pi == heavy ? 1 : 0) : (pi < nb ? 1 : 0);
-  for (int pass = 0; pass < passes; ++pass) {
-    if (pass) __syncthreads();  // every wave is done with the LDS tiles of the first block
-    run_block(pass ? pi : heavy);
+  // Blocks of this workgroup: causal pairs (i, nb-1-i), heavy block first, or single blocks
+  // i, for i = pi, pi + nqb, pi + 2 nqb, ...: the grid covers every block of a sequence of
+  // up to the sized length in one round, and a longer packed sequence (max_seqlen
+  // understated) is still computed in full. One inlined copy of the block body: later
+  // blocks reuse its registers.
+  int i = pi;
+  bool second = false, first = true;
+  for (;;) {
+    const int hi = CAUSAL ? nb - 1 - i : i;
+    if (CAUSAL ? i > hi : i >= nb) break;
+    if (!first) __syncthreads();  // every wave is done with the LDS tiles of the last block
+    first = false;
+    run_block(second ? i : hi);
+    if (CAUSAL && !second && i < hi) {
+      second = true;
+    } else {
+      second = false;
+      i += p.nqb;
+    }
   }
 }
 

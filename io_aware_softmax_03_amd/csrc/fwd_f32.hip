@@ -36,13 +36,15 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args p) {
   __shared__ __attribute__((aligned(16))) float ks[kKT * D];
   __shared__ __attribute__((aligned(16))) float vs[kKT * D];
 
-  const int qb = p.nqb - 1 - (int)(group_id_x() % p.nqb);
+  const int qb_first = p.nqb - 1 - (int)(group_id_x() % p.nqb);
   const int bh = group_id_x() / p.nqb;
   const int h = bh % p.heads, bs = bh / p.heads;
   int seq_start, seq_start_k, L, Lk;  // L: query rows, Lk: keys
   if constexpr (VARLEN) {
-    seq_start = p.cu_seqlens[bs];
-    L = p.cu_seqlens[bs + 1] - seq_start;
+    // offsets clamped into the packed tensor: a sequence starts in [0, T] and ends in
+    // [its start, T], so no access leaves the buffers whatever cu_seqlens holds
+    seq_start = min(max(p.cu_seqlens[bs], 0), p.total_rows);
+    L = min(max(p.cu_seqlens[bs + 1], seq_start), p.total_rows) - seq_start;
     seq_start_k = seq_start;
     Lk = L;
   } else {
@@ -51,8 +53,10 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args p) {
     seq_start_k = bs * p.seqlen_k;
     Lk = p.seqlen_k;
   }
+  // query blocks qb_first, qb_first + nqb, ...: a packed sequence longer than the grid was
+  // sized for (max_seqlen understated) is still computed in full
+  for (int qb = qb_first; qb * RPB < L; qb += p.nqb) {
   const int q0 = qb * RPB;
-  if (q0 >= L) return;
   const size_t rs = (size_t)p.heads * D;      // Q / O row stride
   const size_t rsk = (size_t)p.kv_heads * D;  // K / V row stride
   const size_t base = ((size_t)seq_start * p.heads + h) * D;
@@ -116,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args p) {
     }
     m = m_new;
   }
-  if (!valid) return;
+  if (valid) {
   const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
   for (int c = 0; c < DPL; ++c) p.o[base + (size_t)myq * rs + part * DPL + c] = ov[c] * inv;
@@ -127,6 +131,8 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args p) {
     else
       p.lse[((size_t)bs * p.heads + h) * p.seqlen + myq] = lse;
   }
+  }  // valid
+  }  // query blocks
 }
 
 template <int D, bool CAUSAL, bool VARLEN>

@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import bits_to_f64, dev_bf16, dev_i32, host, max_abs
+from gpu_util import bits_to_f64, dev_bf16, dev_f32, dev_i32, host, max_abs
 
 pytestmark = pytest.mark.gpu
 
@@ -83,3 +83,61 @@ def test_empty_inputs_through_the_binding():
     kc = torch.empty((0, 5, 2, 128), dtype=torch.bfloat16, device="cuda")
     o, lse = fa().decode(qd, kc, kc, num_splits=4)
     assert o.shape == (0, 2, 128) and lse.shape == (0, 2)
+
+
+# ------------------------------------------------------------------ packed-sequence contract
+
+def _varlen_inputs(lengths, H, d, dtype, seed):
+    return [synth.varlen_tensor(seed, t, lengths, H, d, dtype) for t in (synth.TENSOR_Q, synth.TENSOR_K, synth.TENSOR_V)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_varlen_understated_max_seqlen_computes_every_row(dtype, causal):
+    """max_seqlen only sizes the grid: with it far below the longest sequence, the
+    workgroups take the extra query blocks and every row still matches the oracle."""
+    lengths = [700, 50, 1300]
+    H, d = 2, 64
+    q, k, v = _varlen_inputs(lengths, H, d, dtype, 21)
+    cu = synth.cu_seqlens_from_lengths(lengths)
+    to = dev_bf16 if dtype == "bf16" else dev_f32
+    o, lse = fa().fwd_varlen(to(q), to(k), to(v), dev_i32(cu), 100, causal=causal, validate=False)
+    f64 = bits_to_f64 if dtype == "bf16" else (lambda x: x.astype(np.float64))
+    o_ref, lse_ref = oracle.attn_fwd_varlen(f64(q), f64(k), f64(v), cu, 1 / math.sqrt(d), causal)
+    tol_o, tol_l = (2e-2, 1e-3) if dtype == "bf16" else (1e-5, 1e-5)
+    assert max_abs(host(o), o_ref) <= tol_o
+    assert max_abs(host(lse), lse_ref) <= tol_l
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_varlen_clamps_offsets_outside_the_tensor(dtype):
+    """Offsets that break the contract (a negative start, a sequence running past
+    total_tokens) are clamped into the tensor: the rows of the clamped sequences match the
+    oracle on the clamped offsets, and nothing is written past row T (guard rows keep their
+    sentinel)."""
+    import ctypes
+    import torch
+    from io_aware_softmax_03_amd import _clib
+    T, G, H, d = 800, 64, 2, 64
+    bad = np.array([-5, 300, 300, 900], dtype=np.int32)       # sequences [0,300), [300,300), [300,800)
+    clamped = np.array([0, 300, 300, 800], dtype=np.int32)
+    q, k, v = _varlen_inputs([T], H, d, dtype, 22)
+    to = dev_bf16 if dtype == "bf16" else dev_f32
+    tq, tk, tv = to(q), to(k), to(v)
+    sentinel = 7.0
+    o_buf = torch.full((T + G, H, d), sentinel, dtype=tq.dtype, device="cuda")
+    lse_buf = torch.full((H * T + G,), sentinel, dtype=torch.float32, device="cuda")
+    cu = dev_i32(bad)
+    code = _clib.FA_DTYPE_BF16 if dtype == "bf16" else _clib.FA_DTYPE_F32
+    st = _clib.lib().fa_fwd_varlen(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), o_buf.data_ptr(), lse_buf.data_ptr(),
+                                   cu.data_ptr(), 3, T, 500, H, H, d, 1 / math.sqrt(d), 1, code,
+                                   ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == _clib.FA_OK
+    torch.cuda.synchronize()
+    o, lse = host(o_buf[:T]), host(lse_buf[:H * T]).reshape(H, T)
+    assert np.all(host(o_buf[T:]) == sentinel) and np.all(host(lse_buf[H * T:]) == sentinel)
+    f64 = bits_to_f64 if dtype == "bf16" else (lambda x: x.astype(np.float64))
+    o_ref, lse_ref = oracle.attn_fwd_varlen(f64(q), f64(k), f64(v), clamped, 1 / math.sqrt(d), True)
+    tol_o, tol_l = (2e-2, 1e-3) if dtype == "bf16" else (1e-5, 1e-5)
+    assert max_abs(o, o_ref) <= tol_o
+    assert max_abs(lse, lse_ref) <= tol_l
