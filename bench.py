@@ -35,6 +35,10 @@ PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
 PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS  # dense e4m3 matrix-core peak (5.0 PFLOP/s)
 SETTLE_S = 0.25  # untimed calls before each secondary workload's warm-up
+# other (non-transcendental) VALU lane-operations per formed score of the d=64 packed forward,
+# from its SQ counters (SQ_INSTS_VALU - SQ_INSTS_VALU_TRANS_F32 per formed score x 64 lanes;
+# profiles/fwd_bwd_counters.md)
+VALU_OPS_PER_SCORE_D64 = 4.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_causal_b2_h16_n8192_d128_traffic.json")
 FWD_SOURCE = os.path.join(ROOT, "io_aware_softmax_03_amd", "csrc", "fwd_bf16.hip")
 
@@ -159,9 +163,20 @@ def extra_measurements(steps, only=None):
         q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
         wall, ev, best = time_launches(lambda: fa.fwd_varlen(q, k, v, cu, max(lengths), causal=True), steps, 3, SETTLE_S)
         fl = costs.varlen_fwd_flops(lengths, H, d, True)
-        out["varlen_causal_16seq_h32_d64"] = {"ms": round(ev, 4), "tflops": round(fl / ev / 1e9, 2),
-                                              "frac_mfma_peak": round(fl / ev / 1e9 / PEAK_BF16_TFLOPS, 4),
-                                              "total_tokens": T}
+        # both rooflines of this d=64 launch over the scores the kernel forms (masked ones
+        # in diagonal blocks included): matrix core (4*d FLOP per score, plus the row-sum
+        # MFMAs, 1/8 of the 32x32x16 time at d=64) and VALU (per score one v_exp_f32 and
+        # VALU_OPS_PER_SCORE other lane-operations, counted on this kernel by the SQ
+        # counters), each at its unit's nominal rate at 2.4 GHz
+        scores = costs.fwd_computed_scores(lengths, H, True)
+        t_mfma = costs.mfma_bound_seconds(scores, d, 1 / 8) * 1e3
+        t_valu = costs.valu_bound_seconds(scores, 1.0, VALU_OPS_PER_SCORE_D64) * 1e3
+        out["varlen_causal_16seq_h32_d64"] = {
+            "ms": round(ev, 4), "tflops": round(fl / ev / 1e9, 2),
+            "frac_mfma_peak": round(fl / ev / 1e9 / PEAK_BF16_TFLOPS, 4), "total_tokens": T,
+            "formed_scores": scores, "mfma_bound_ms": round(t_mfma, 4), "valu_bound_ms": round(t_valu, 4),
+            "frac_of_mfma_bound": round(t_mfma / ev, 4), "frac_of_valu_bound": round(t_valu / ev, 4),
+            "valu_per_score": f"1 exp (quarter rate) + {VALU_OPS_PER_SCORE_D64} other VALU ops (full rate)"}
         del q, k, v
 
 
@@ -290,6 +305,7 @@ def extra_measurements(steps, only=None):
 
 
 def main():
+    global SETTLE_S
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
@@ -300,10 +316,13 @@ def main():
                          "decode_gqa, decode_paged); for profiler runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--settle-s", type=float, default=SETTLE_S,
+                    help="untimed seconds of calls before each secondary workload (0 for profiler runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (untimed), so that a counter "
                          "profile of this command holds a kernel of known traffic to scale HBM counters by")
     args = ap.parse_args()
+    SETTLE_S = args.settle_s
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this library has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)

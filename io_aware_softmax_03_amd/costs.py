@@ -143,3 +143,41 @@ def band_tiles_visited(nq, nk, block_q, block_k, causal, window_left=-1, window_
         lo, hi = min(a for a, _ in ranges), max(b for _, b in ranges)
         tiles.extend((qb, kb) for kb in range(lo // block_k, hi // block_k + 1))
     return tiles
+
+
+def fwd_computed_scores(lengths, H, causal, rows_per_wave=32, keys_per_block=32):
+    """(query, key) scores the bf16 forward kernel forms, masked ones included: per sequence
+    and head, each wave of rows_per_wave query rows forms whole blocks of keys_per_block
+    keys, up to the block holding its last row's last visible key (all blocks when not
+    causal). Useful work is fewer: the diagonal blocks are partly masked."""
+    total = 0
+    for L in lengths:
+        per_head = 0
+        for qw in range(0, L, rows_per_wave):
+            last = min(qw + rows_per_wave, L) - 1 if causal else L - 1
+            per_head += (last // keys_per_block + 1) * keys_per_block * rows_per_wave
+        total += per_head * H
+    return total
+
+
+# Per-SIMD issue rates of gfx950 from its unit counts (256 CUs x 4 SIMDs at 2.4 GHz): the
+# fp32 vector peak of 157.3 TFLOP/s is 32 FMA lanes per clock per SIMD, so a wave64 VALU
+# instruction takes 2 cycles; transcendental instructions (v_exp_f32) run at a quarter of
+# that rate, 8 cycles; a 32x32x16 bf16 MFMA takes 32 cycles (1024 FLOP per clock).
+VALU_CYCLES, TRANS_CYCLES, MFMA_32X32X16_CYCLES = 2.0, 8.0, 32.0
+N_SIMD, CLOCK_HZ = 1024, 2.4e9
+
+
+def valu_bound_seconds(scores, exp_per_score, other_valu_per_score):
+    """Lower bound on a launch's time from its VALU work: per score, exp_per_score
+    transcendental and other_valu_per_score other lane-operations, at the full-rate and
+    quarter-rate VALU throughput of every SIMD at 2.4 GHz."""
+    cycles = scores / 64.0 * (exp_per_score * TRANS_CYCLES + other_valu_per_score * VALU_CYCLES)
+    return cycles / N_SIMD / CLOCK_HZ
+
+
+def mfma_bound_seconds(scores, d, extra_mfma_fraction=0.0):
+    """Lower bound on a launch's time from its matrix-core work: 4*d FLOP per formed score
+    (S = Q K^T and O += P V), plus a fraction of extra MFMA time (e.g. row sums), at the
+    dense bf16 peak."""
+    return scores * 4.0 * d * (1.0 + extra_mfma_fraction) / (N_SIMD * 1024.0 * CLOCK_HZ)
