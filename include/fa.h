@@ -37,7 +37,9 @@
  *   Head dim d must be 64 or 128.
  *   Memory   every pointer is device memory owned by the caller; the library
  *            allocates nothing and keeps no state between calls. Workspaces
- *            are passed in after a size query.
+ *            are passed in after a size query. The one exception is
+ *            fa_decode_noalloc, whose partials live in a fixed scratch array
+ *            of the library (one per GPU, for the life of the process).
  *   Streams  `stream` is a hipStream_t (NULL = the default stream). Calls only
  *            enqueue kernels on that stream: no host synchronisation and no
  *            device-to-host copy. Results are ready when the stream is.
