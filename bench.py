@@ -39,6 +39,7 @@ SETTLE_S = 0.25  # untimed calls before each secondary workload's warm-up
 # from its SQ counters (SQ_INSTS_VALU - SQ_INSTS_VALU_TRANS_F32 per formed score x 64 lanes;
 # profiles/fwd_bwd_counters.md)
 VALU_OPS_PER_SCORE_D64 = 4.0
+FWD_ROWS_PER_WAVE_D64 = 64  # the d=64 forward's waves own 64 query rows (two 32-row groups)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_causal_b2_h16_n8192_d128_traffic.json")
 FWD_SOURCE = os.path.join(ROOT, "io_aware_softmax_03_amd", "csrc", "fwd_bf16.hip")
 
@@ -170,7 +171,7 @@ def extra_measurements(steps, only=None):
         # MFMAs, 1/8 of the 32x32x16 time at d=64) and VALU (per score one v_exp_f32 and
         # VALU_OPS_PER_SCORE other lane-operations, counted on this kernel by the SQ
         # counters), each at its unit's nominal rate at 2.4 GHz
-        scores = costs.fwd_computed_scores(lengths, H, True)
+        scores = costs.fwd_computed_scores(lengths, H, True, rows_per_wave=FWD_ROWS_PER_WAVE_D64)
         t_mfma = costs.mfma_bound_seconds(scores, d, 1 / 8) * 1e3
         t_valu = costs.valu_bound_seconds(scores, 1.0, VALU_OPS_PER_SCORE_D64) * 1e3
         out["varlen_causal_16seq_h32_d64"] = {

@@ -3,12 +3,14 @@
 // Method ("FlashAttention: IO-aware exact attention", "Tile decomposition" and "Online
 // softmax"; "FlashAttention-2 and -3", "Fewer non-matmul FLOPs", "Parallelism over the
 // sequence", "Split the queries, not the keys"):
-//   * one workgroup of eight waves per (query block of 256 rows, batch*head), two waves per
-//     SIMD; the query block stays in registers while 32-key blocks of K and V stream through
-//     LDS (double buffered) and are shared by the eight waves;
-//   * each wave owns 32 whole query rows, so the running max, running sum and output
-//     accumulator of a row never leave the wave (the code is written for NG = kQW / 32
-//     query groups per wave, each K or V operand read from LDS feeding NG MFMAs);
+//   * one workgroup per (query block of 256 rows, batch*head), two waves per SIMD: for
+//     d = 128 eight waves of 32 rows (one workgroup per CU), for d = 64 four waves of 64 rows
+//     (two workgroups per CU, each with its own barriers); the query block stays in
+//     registers while 32-key blocks of K and V stream through LDS (double buffered) and are
+//     shared by the workgroup's waves;
+//   * each wave owns whole query rows, so the running max, running sum and output
+//     accumulator of a row never leave the wave (NG = kQW / 32 query groups per wave, each
+//     K or V operand read from LDS feeding NG MFMAs);
 //   * scores are computed transposed, S^T = K Q^T, so the 32 keys x 32 queries MFMA output
 //     leaves one query per lane (16 scores, the other 16 in the lane 32 away) and the row
 //     max / row sum are in-lane plus one swap between wave halves;
@@ -43,10 +45,19 @@ namespace fa {
 namespace {
 
 constexpr int kBC = 32;       // keys per streamed block
-constexpr int kNW = 8;        // waves per workgroup (two per SIMD)
-constexpr int kQW = 32;       // query rows per wave
-constexpr int NG = kQW / 32;  // 32-row query groups per wave
-constexpr int kBR = kNW * kQW;
+// Waves per workgroup and query rows per wave. d = 128: eight waves of 32 rows, one
+// workgroup per CU (the 32 x 128 output accumulator of a wave takes 64 of its 256
+// registers). d = 64: four waves of 64 rows (two query groups per wave, so each K or V
+// operand read from LDS feeds two MFMAs), two workgroups per CU; on the packed d = 64
+// workload 0.40 ms against 0.51 ms for eight 32-row waves, whose barriers coupled all the
+// waves of a CU.
+template <int D>
+struct FwdShape {
+  static constexpr int NW = D == 64 ? 4 : 8;
+  static constexpr int QW = D == 64 ? 64 : 32;
+  static constexpr int BR = NW * QW;            // query rows per block
+  static constexpr int WG_PER_CU = 8 / NW;      // workgroups per CU at two waves per SIMD
+};
 constexpr float kRescaleThreshold = 8.0f;  // log2 units, for a wave's first block: P <= 256
 // Bound on P after the first block. The result is exact for any pivot; the bound only keeps
 // the fp32 accumulators far from overflow (O <= 2^16 * keys * max|V|). A larger bound than
@@ -112,7 +123,11 @@ __device__ __forceinline__ bf16x8 scale_bf16x8(const bf16x8& x, float alpha) {
 }
 
 template <int D, bool CAUSAL, bool VARLEN, bool WINDOW>
-__global__ __launch_bounds__(kNW * 64, 1) void fwd_bf16_kernel(FwdKernelArgs p) {
+__global__ __launch_bounds__(FwdShape<D>::NW * 64, FwdShape<D>::WG_PER_CU) void fwd_bf16_kernel(FwdKernelArgs p) {
+  constexpr int kNW = FwdShape<D>::NW;  // waves per workgroup
+  constexpr int kQW = FwdShape<D>::QW;  // query rows per wave
+  constexpr int NG = kQW / 32;          // 32-row query groups per wave
+  constexpr int kBR = FwdShape<D>::BR;
   constexpr int KK = D / 16;                 // MFMA k-steps over the head dim
   constexpr int DB = D / 32;                 // 32-wide output blocks over the head dim
   constexpr int KS = kBC / 16;               // MFMA k-steps over a key block
@@ -812,14 +827,14 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.lo_off = a.lo_off;
   p.hi_off = a.hi_off;
   p.total_rows = a.total_rows;
-  const int nqb = (a.seqlen + kBR - 1) / kBR;
+  const int nqb = (a.seqlen + FwdShape<D>::BR - 1) / FwdShape<D>::BR;
   p.nqb = CAUSAL ? (nqb + 1) / 2 : nqb;  // causal workgroups take a pair of query blocks
   p.scale_log2 = a.scale * kLog2e;
   const long long blocks = (long long)p.nqb * a.heads * a.batch;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   p.grid = (int)blocks;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, VARLEN, WINDOW>), dim3((unsigned)blocks), dim3(kNW * 64), 0, stream, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, VARLEN, WINDOW>), dim3((unsigned)blocks), dim3(FwdShape<D>::NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
