@@ -38,7 +38,7 @@ SETTLE_S = 0.25  # untimed calls before each secondary workload's warm-up
 # other (non-transcendental) VALU lane-operations per formed score of the d=64 packed forward,
 # from its SQ counters (SQ_INSTS_VALU - SQ_INSTS_VALU_TRANS_F32 per formed score x 64 lanes;
 # profiles/fwd_bwd_counters.md)
-VALU_OPS_PER_SCORE_D64 = 4.0
+VALU_OPS_PER_SCORE_D64 = 3.8
 FWD_ROWS_PER_WAVE_D64 = 64  # the d=64 forward's waves own 64 query rows (two 32-row groups)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_causal_b2_h16_n8192_d128_traffic.json")
 FWD_SOURCE = os.path.join(ROOT, "io_aware_softmax_03_amd", "csrc", "fwd_bf16.hip")
