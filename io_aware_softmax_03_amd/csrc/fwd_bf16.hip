@@ -56,7 +56,6 @@ struct FwdShape {
   static constexpr int NW = D == 64 ? 4 : 8;
   static constexpr int QW = D == 64 ? 64 : 32;
   static constexpr int BR = NW * QW;            // query rows per block
-  static constexpr int WG_PER_CU = 8 / NW;      // workgroups per CU at two waves per SIMD
 };
 constexpr float kRescaleThreshold = 8.0f;  // log2 units, for a wave's first block: P <= 256
 // Bound on P after the first block. The result is exact for any pivot; the bound only keeps
@@ -123,7 +122,8 @@ __device__ __forceinline__ bf16x8 scale_bf16x8(const bf16x8& x, float alpha) {
 }
 
 template <int D, bool CAUSAL, bool VARLEN, bool WINDOW>
-__global__ __launch_bounds__(FwdShape<D>::NW * 64, FwdShape<D>::WG_PER_CU) void fwd_bf16_kernel(FwdKernelArgs p) {
+// (the second bound is the minimum number of waves per SIMD: two, 256 registers each)
+__global__ __launch_bounds__(FwdShape<D>::NW * 64, 2) void fwd_bf16_kernel(FwdKernelArgs p) {
   constexpr int kNW = FwdShape<D>::NW;  // waves per workgroup
   constexpr int kQW = FwdShape<D>::QW;  // query rows per wave
   constexpr int NG = kQW / 32;          // 32-row query groups per wave
