@@ -225,12 +225,33 @@ def extra_measurements(steps, only=None):
 
 
     def _f32():
-        # fp32 forward, B=1 H=1 N=256 d=64 (launch-latency bound)
+        # fp32 forward, B=1 H=1 N=256 d=64 (latency bound: one 256-key block per workgroup).
+        # "us": HIP events around each call (host launch cost included: the kernel is shorter
+        # than a call's host work); "us_graph": per call inside a replayed HIP graph of 64
+        # calls, the kernel's own duration plus the gap between graph nodes
         gen.manual_seed(1)
         q, k, v = (torch.randn((1, 256, 1, 64), generator=gen, device="cuda") for _ in range(3))
-        wall, ev, best = time_launches(lambda: fa.fwd(q, k, v), steps, 3, SETTLE_S)
-        out["fwd_f32_n256_d64"] = {"us": round(ev * 1e3, 2)}
-        del q, k, v
+        o = torch.empty_like(q)
+        lse = torch.empty((1, 1, 256), dtype=torch.float32, device="cuda")
+        wall, ev, best = time_launches(lambda: fa.fwd(q, k, v, out=(o, lse)), steps, 3, SETTLE_S)
+        o_eager = o.clone()
+        calls = 64
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fa.fwd(q, k, v, out=(o, lse))
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(calls):
+                fa.fwd(q, k, v, out=(o, lse))
+        o.zero_()
+        torch.cuda.synchronize()
+        gwall, gev, gbest = time_launches(graph.replay, max(10, steps // 10), 3)
+        if not torch.equal(o, o_eager):
+            raise RuntimeError("fp32 forward: graph replay differs from the eager call")
+        out["fwd_f32_n256_d64"] = {"us": round(ev * 1e3, 2), "us_graph": round(gev * 1e3 / calls, 2)}
+        del q, k, v, o, lse, graph
 
 
     def _decode():

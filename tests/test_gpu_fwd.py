@@ -34,6 +34,10 @@ def gen_dense(seed, B, N, H, d, dtype):
     (2, 100, 3, 128, True),
     (1, 257, 2, 64, False),
     (1, 1, 1, 128, True),
+    (1, 1000, 4, 64, True),     # several 256-key blocks, ragged tail, four-row query blocks
+    (1, 600, 4, 128, True),     # four-row query blocks at d = 128
+    (2, 1024, 4, 128, False),   # eight-row query blocks (the larger grid), four key blocks
+    (1, 2048, 2, 64, True),     # eight-row query blocks, causal over eight key blocks
 ])
 def test_fwd_f32(B, N, H, d, causal):
     q, k, v = gen_dense(1, B, N, H, d, "f32")
