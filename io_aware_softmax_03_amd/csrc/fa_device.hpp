@@ -63,6 +63,17 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
+
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>());
+    static_for<B + 1, E>(f);
+  }
+}
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Round-to-nearest-even fp32 -> bf16 of two values (one v_cvt_pk_bf16_f32), lo first.

@@ -98,17 +98,6 @@ __device__ __forceinline__ int swz_v(int row) {
   return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
-__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
-
-// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
-template <int B, int E, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>());
-    static_for<B + 1, E>(f);
-  }
-}
-
 // x * alpha, element-wise, rounded back to bf16
 __device__ __forceinline__ bf16x8 scale_bf16x8(const bf16x8& x, float alpha) {
   const u32x4 w = __builtin_bit_cast(u32x4, x);

@@ -13,14 +13,15 @@
 //    transposed, [B, H, block, d, 64], with the keys of a block in the order the attention
 //    kernel's P registers hold them, so each lane's V^T operand is 32 contiguous bytes.
 // 2. fwd_fp8_kernel: 4 waves of 32 query rows per workgroup, two workgroups per CU (about
-//    200 registers a wave), so one wave's softmax runs beside another's matrix-core work.
-//    Per 64-key block the K and V^T tiles (contiguous 8 KB blocks of the workspace) are
-//    copied straight into LDS one block ahead and shared by the four waves; S^T = K Q^T
-//    and O^T += V^T P^T run on v_mfma_scale_f32_32x32x64_f8f6f4, the online softmax in
-//    fp32 (base 2), and P is quantized to e4m3 as P * 2^8 (formed directly as
-//    2^(s - m + 8)). The block scales enter exactly: 2^(eq + ek) on the score scale, 2^ev and
-//    2^-8 through the MFMA's E8M0 operand scales. The row sum and the LSE use the
-//    unquantized P.
+//    220 registers a wave). Per 64-key block the K and V^T tiles (contiguous 8 KB blocks of
+//    the workspace) are copied straight into LDS (K two blocks ahead, V^T one) and shared by
+//    the four waves; S^T = K Q^T and O^T += V^T P^T run on
+//    v_mfma_scale_f32_32x32x64_f8f6f4, the online softmax in fp32 (base 2), and P is
+//    quantized to e4m3 as P * 2^8 (formed directly as 2^(s - m + 8)). Within a wave the
+//    work is pipelined over three blocks: step j forms S(j+1) and multiplies P(j-1) into O on
+//    the matrix core while the VALU forms the codes of P(j) (exact running maximum, so
+//    P <= 1). The block scales enter exactly: 2^(eq + ek) on the score scale, 2^ev and 2^-8
+//    through the MFMA's E8M0 operand scales. The row sum and the LSE use the unquantized P.
 //
 // Operand layouts of v_mfma_scale_f32_32x32x64_f8f6f4 with e4m3 operands (lane l, r = l%32,
 // hh = l/32): A row r, B column r; the 32 bytes of a lane are 32 of the 64 k indices, and A
@@ -214,6 +215,13 @@ struct AttnArgs {
   float c2;            // scale * log2(e), divided by d when Q and K were rotated
 };
 
+// v_max3_f32 as one instruction (plain fmaxf chains are not always fused)
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, const f32x16& c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
@@ -253,8 +261,11 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(AttnArgs p) {
   const uint8_t* qhead = p.q8 + ((size_t)bs * p.heads + h) * Np * D;
   const uint8_t* khead = p.k8 + ((size_t)bs * p.kv_heads + hk) * Np * D;
   const uint8_t* vhead = p.v8t + ((size_t)bs * p.kv_heads + hk) * Np * D;
-  const int* __restrict__ ekp = p.ek + ((size_t)bs * p.kv_heads + hk) * p.nblk;
-  const int* __restrict__ evp = p.ev + ((size_t)bs * p.kv_heads + hk) * p.nblk;
+  // block exponents of K and V, read through the constant address space so that the
+  // per-step reads are scalar loads (written by the quantization launches before this one)
+  typedef const __attribute__((address_space(4))) int cint;
+  cint* ekp = (cint*)(p.ek + ((size_t)bs * p.kv_heads + hk) * p.nblk);
+  cint* evp = (cint*)(p.ev + ((size_t)bs * p.kv_heads + hk) * p.nblk);
 
   const int tid = thread_id_x();
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -301,16 +312,22 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(AttnArgs p) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qf[ks] = active ? *(const i32x8*)(qhead + (size_t)(qw + r) * D + 64 * ks + 32 * hh) : i32x8{};
+    // pinned here, before the key loop, so the loads are not sunk into it
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[ks]));
 
-    auto issue = [&](auto bufc, int kb) {
-      const __amdgpu_buffer_rsrc_t ks_ = make_rsrc(khead + (size_t)kb * TILE, TILE);
-      const __amdgpu_buffer_rsrc_t vs_ = make_rsrc(vhead + (size_t)kb * TILE, TILE);
-      char* kd = kbuf(bufc) + wid * LOADS * 1024;
-      char* vd = vbuf(bufc) + wid * LOADS * 1024;
+    // copies of key block kb into buffer BUF: K (row-major) and V^T tiles, each wave its share
+    auto issue_k = [&](auto bufc, int kb) {
+      const __amdgpu_buffer_rsrc_t src = make_rsrc(khead + (size_t)kb * TILE, TILE);
+      char* dst = kbuf(bufc) + wid * LOADS * 1024;
 #pragma unroll
-      for (int it = 0; it < LOADS; ++it) copy16_to_lds(ks_, k_src[it], kd + it * 1024);
+      for (int it = 0; it < LOADS; ++it) copy16_to_lds(src, k_src[it], dst + it * 1024);
+    };
+    auto issue_v = [&](auto bufc, int kb) {
+      const __amdgpu_buffer_rsrc_t src = make_rsrc(vhead + (size_t)kb * TILE, TILE);
+      char* dst = vbuf(bufc) + wid * LOADS * 1024;
 #pragma unroll
-      for (int it = 0; it < LOADS; ++it) copy16_to_lds(vs_, v_src[it], vd + it * 1024);
+      for (int it = 0; it < LOADS; ++it) copy16_to_lds(src, v_src[it], dst + it * 1024);
     };
     auto read8 = [](const char* base, int o0, int o1) {
       const u32x4 a = *(const u32x4*)(base + o0);
@@ -318,6 +335,8 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(AttnArgs p) {
       return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
     };
 
+    // running maximum (log2 units of the scaled score; P in (0, 1]), this lane's half of the
+    // running row sum of P, and O^T
     float m = -1e30f, l = 0.f;
     f32x16 oacc[DB];
 #pragma unroll
@@ -325,55 +344,32 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(AttnArgs p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
 
-    auto compute = [&](auto bufc, int kb) {
+    // value 16t + i of a score block: S^T[key kb*64 + 32t + 8(i/4) + 4hh + i%4][query qw + r]
+    auto edge = [&](int kb) { return (CAUSAL && kb * kRows + kRows - 1 > qw) || kb * kRows + kRows > N; };
+    auto mask = [&](f32x16 (&s)[2], int kb) {
+      const int q = qw + r;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb * kRows + 32 * t + 8 * (i >> 2) + 4 * hh + (i & 3);
+          if ((CAUSAL && key > q) || key >= N) s[t][i] = -INFINITY;
+        }
+    };
+    // S^T = K Q^T of one block from K buffer BUF (the first block, before the loop)
+    auto qk = [&](f32x16 (&s)[2], auto bufc) {
       const char* kb_ = kbuf(bufc);
-      const char* vb_ = vbuf(bufc);
-      const float cs = __builtin_amdgcn_ldexpf(p.c2, eq + ekp[kb]);
-      const int sv = evp[kb] + 127;
-      // value 16t + 4i + j: score of key kb*64 + 32t + 8i + 4hh + j, query qw + r
-      float s[32];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        f32x16 st = mfma_f8(read8(kb_, k_off[t][0][0], k_off[t][0][1]), qf[0], f32x16{}, 127, 127);
+        s[t] = mfma_f8(read8(kb_, k_off[t][0][0], k_off[t][0][1]), qf[0], f32x16{}, 127, 127);
 #pragma unroll
-        for (int ks = 1; ks < KS; ++ks)
-          st = mfma_f8(read8(kb_, k_off[t][ks][0], k_off[t][ks][1]), qf[ks], st, 127, 127);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[16 * t + i] = st[i];
+        for (int ks = 1; ks < KS; ++ks) s[t] = mfma_f8(read8(kb_, k_off[t][ks][0], k_off[t][ks][1]), qf[ks], s[t], 127, 127);
       }
-      if ((CAUSAL && kb * kRows + kRows - 1 > qw) || kb * kRows + kRows > N) {
-        const int q = qw + r;
-#pragma unroll
-        for (int v = 0; v < 32; ++v) {
-          const int key = kb * kRows + 32 * (v >> 4) + 8 * ((v >> 2) & 3) + 4 * hh + (v & 3);
-          if ((CAUSAL && key > q) || key >= N) s[v] = -INFINITY;
-        }
-      }
-      // the scale is positive: the maximum of the raw scores gives that of the scaled ones
-      float mx = s[0];
-#pragma unroll
-      for (int v = 1; v < 32; ++v) mx = fmaxf(mx, s[v]);
-      mx = pair_max(mx) * cs;
-      const float m_new = fmaxf(m, mx);
-      if (wave_any(m_new > m)) {
-        const float alpha = exp2_fast(m - m_new);
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-        m = m_new;
-      }
-      // P * 2^8 directly: 2^(s cs - m + 8); the row sum takes P = that * 2^-8
-      const float mm = m - (float)kPScaleLog2;
-      float ps = 0.f;
-#pragma unroll
-      for (int v = 0; v < 32; ++v) {
-        s[v] = exp2_fast(__builtin_fmaf(s[v], cs, -mm));
-        ps += s[v];
-      }
-      l = __builtin_fmaf(ps, 1.0f / (1 << kPScaleLog2), l);
-      i32x8 pb;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) pb[c] = (int)cvt4_fp8(s[4 * c], s[4 * c + 1], s[4 * c + 2], s[4 * c + 3], 0);
+    };
+    // O^T += V^T P^T of the wave's last block, on its own
+    auto pv_tail = [&](const i32x8& pb, auto bufc, int kb) {
+      const char* vb_ = vbuf(bufc);
+      const int sv = evp[kb] + 127;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
         oacc[db] = mfma_f8(read8(vb_, v_off[db][0], v_off[db][1]), pb, oacc[db], sv, 127 - kPScaleLog2);
@@ -381,19 +377,185 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(AttnArgs p) {
 
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
-    auto step = [&](auto bufc, int kb) {
-      if (kb + 1 < nkb) issue(std::integral_constant<int, decltype(bufc)::value ^ 1>(), kb + 1);
-      if (kb < nkw) compute(bufc, kb);
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of block kb + 1 have landed
-      __syncthreads();                // ... and everyone's; block kb is free for reuse
+
+    // ---- step j (parity PH = j & 1) of a wave, for j < nkw: copies K(j+2) -> K buffer j&1
+    // and V(j) -> V buffer j&1; forms S(j+1) = K(j+1) Q^T from K buffer !(j&1) on the matrix
+    // core beside the softmax of block j (maximum, exponentials, sums, e4m3 codes of P(j)), then
+    // O^T += V(j-1)^T P(j-1)^T from V buffer !(j&1). O is rescaled by the step's factor once
+    // the P(j-1) product (formed against the previous maximum) is in. Past the last block the
+    // K copies repeat it (that buffer is free and never read), so a step has no branches.
+    //
+    // The step is laid out as NSLOT slots of one MFMA each (the score MFMAs first), fenced by
+    // scheduling barriers; each slot carries VPS probabilities' worth of VALU work (scale FMA,
+    // exponential, sum, conversion) and the LDS operand reads of the MFMA two slots on.
+    constexpr int NQK = 2 * KS;            // score MFMAs: two 32-key halves x head-dim k-steps
+    constexpr int NSLOT = NQK + DB;        // + P V MFMAs
+    constexpr int VPS = 32 / NSLOT;        // probabilities per slot (4 at d = 128, 8 at d = 64)
+    constexpr int AH = 1;                  // operand reads, slots ahead of their MFMA
+    static_assert(32 % NSLOT == 0, "slot plan");
+    auto fma_slot = [](int v) { return v / VPS - 1 < -1 ? -1 : v / VPS - 1; };
+    auto exp_slot = [](int v) { return v / VPS; };
+    auto add_slot = [](int v) { return v / VPS + 1 < NSLOT ? v / VPS + 1 : NSLOT; };
+    auto cvt_slot = [](int qd) { return (4 * qd + 3) / VPS + 1 < NSLOT ? (4 * qd + 3) / VPS + 1 : NSLOT; };
+    auto read_slot = [](int u) { return u - AH < -1 ? -1 : u - AH; };
+
+    f32x16 sA[2], sB[2];
+    i32x8 pA = i32x8{}, pB = i32x8{};
+    float cs_cur = 0.f;  // score factor of block j: scale log2(e) 2^(eq + ek[j])
+
+    auto step = [&](auto phase, int j) {
+      constexpr int PH = decltype(phase)::value;
+      constexpr bool ODD = PH & 1;
+      f32x16(&c)[2] = ODD ? sB : sA;  // S(j)
+      f32x16(&n)[2] = ODD ? sA : sB;  // S(j+1)
+      i32x8& pc = ODD ? pB : pA;      // P(j)
+      i32x8& pp = ODD ? pA : pB;      // P(j-1)
+      const char* kb_ = kbuf(std::integral_constant<int, PH + 1>());  // K(j+1)
+      const char* vb_ = vbuf(std::integral_constant<int, PH + 1>());  // V(j-1)
+      const int sv = j > 0 ? evp[j - 1] + 127 : 127;
+      const int ek_next = ekp[min(j + 1, p.nblk - 1)];
+
+      // preamble: mask, block maximum, new running maximum and factor
+      if (edge(j)) mask(c, j);
+      float mx;
+      {
+        float a0 = vmax3(c[0][0], c[0][1], c[0][2]), a1 = vmax3(c[1][0], c[1][1], c[1][2]);
+#pragma unroll
+        for (int i = 3; i < 15; i += 2) {
+          a0 = vmax3(a0, c[0][i], c[0][i + 1]);
+          a1 = vmax3(a1, c[1][i], c[1][i + 1]);
+        }
+        a0 = vmax3(a0, c[0][15], c[1][15]);
+        mx = pair_max(fmaxf(a0, a1)) * cs_cur;
+      }
+      const float m_new = fmaxf(m, mx);
+      const bool grow = wave_any(m_new > m);
+      const float alpha = exp2_fast(m - m_new);
+      l *= alpha;
+      m = m_new;
+      const float mm = m - (float)kPScaleLog2;  // codes are P * 2^8 = 2^(s cs - m + 8)
+      const float cs = cs_cur;
+
+      i32x8 op[NSLOT];
+      float acc[4];
+      uint32_t code[8];
+      auto slot = [&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        // LDS operand reads
+#pragma unroll
+        for (int u = 0; u < NSLOT; ++u) {
+          if (read_slot(u) == t) {
+            if (u < NQK)
+              op[u] = read8(kb_, k_off[u / KS][u % KS][0], k_off[u / KS][u % KS][1]);
+            else
+              op[u] = read8(vb_, v_off[u - NQK][0], v_off[u - NQK][1]);
+          }
+        }
+        // the slot's MFMA
+        if constexpr (t >= 0 && t < NQK) {
+          constexpr int tt = t / KS, ks = t % KS;
+          n[tt] = mfma_f8(op[t], qf[ks], ks == 0 ? f32x16{} : n[tt], 127, 127);
+        } else if constexpr (t >= NQK && t < NSLOT) {
+          constexpr int db = t - NQK;
+          oacc[db] = mfma_f8(op[t], pp, oacc[db], sv, 127 - kPScaleLog2);
+        }
+        // VALU work on P(j)
+#pragma unroll
+        for (int v = 0; v < 32; ++v) {
+          const int tt = v / 16, i = v % 16;
+          if (fma_slot(v) == t) c[tt][i] = __builtin_fmaf(c[tt][i], cs, -mm);
+          if (exp_slot(v) == t) c[tt][i] = exp2_fast(c[tt][i]);
+          if (add_slot(v) == t) acc[v % 4] = v < 4 ? c[tt][i] : acc[v % 4] + c[tt][i];
+        }
+#pragma unroll
+        for (int qd = 0; qd < 8; ++qd) {
+          if (cvt_slot(qd) == t) {
+            const int tt = qd / 4, i = 4 * (qd % 4);
+            // (both halves of the register are written: its old contents, P(j-2)'s codes,
+            // need no clearing)
+            int w = __builtin_amdgcn_cvt_pk_fp8_f32(c[tt][i], c[tt][i + 1], pc[qd], false);
+            code[qd] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[tt][i + 2], c[tt][i + 3], w, true);
+            asm volatile("" : "+v"(code[qd]));  // keeps the conversion in its slot
+          }
+        }
+        // the sums stay in their slots too (sunk, they all landed in the next step's tail)
+        if constexpr (t >= 1) asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
+        __builtin_amdgcn_sched_barrier(0);
+      };
+
+      slot(std::integral_constant<int, -1>());
+      issue_k(std::integral_constant<int, PH>(), min(j + 2, nkb - 1));
+      issue_v(std::integral_constant<int, PH>(), j);
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<0, NSLOT + 1>(slot);
+
+      // tail: the codes of P(j), the row sum, O rescaled past the P(j-1) product. S(j+1) is
+      // pinned here: the IR optimisers would otherwise sink its MFMAs past the barrier, next
+      // to their first use in the following step, out of the slots that overlap them with the
+      // softmax.
+      asm volatile("" : "+v"(n[0]), "+v"(n[1]));
+#pragma unroll
+      for (int qd = 0; qd < 8; ++qd) pc[qd] = (int)code[qd];
+      l = __builtin_fmaf((acc[0] + acc[1]) + (acc[2] + acc[3]), 1.0f / (1 << kPScaleLog2), l);
+      if (grow) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      }
+      cs_cur = __builtin_amdgcn_ldexpf(p.c2, eq + ek_next);
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of K(j+2), V(j) have landed
+      __syncthreads();                // ... and everyone's; K(j), V(j-2) buffers are free
     };
-    issue(B0(), 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int kb = 0; kb < nkb; kb += 2) {
-      step(B0(), kb);
-      if (kb + 1 < nkb) step(B1(), kb + 1);
+    // a step of a wave past its last key block: its share of the copies, and the barrier
+    auto idle_step = [&](auto phase, int j) {
+      constexpr int PH = decltype(phase)::value;
+      issue_k(std::integral_constant<int, PH>(), min(j + 2, nkb - 1));
+      issue_v(std::integral_constant<int, PH>(), j);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    };
+    using F0 = std::integral_constant<int, 0>;
+    using F1 = std::integral_constant<int, 1>;
+
+    // ---- prologue: K(0) -> K buffer 0, K(1) -> K buffer 1; V buffer 1 is cleared, so the
+    // first step's P V (zero codes of P(-1) times that buffer) adds exact zeros
+    if (nkb > 0) {
+      issue_k(B0(), 0);
+      issue_k(B1(), min(1, nkb - 1));
+      {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int o = tid * 16; o < TILE; o += 256 * 16) *(u32x4*)(v_lds1 + o) = z;
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (nkw > 0) {
+        qk(sA, B0());
+        cs_cur = __builtin_amdgcn_ldexpf(p.c2, eq + ekp[0]);
+      }
+      __syncthreads();  // every wave is done with K(0)
+
+      int j = 0;
+      if (nkw > 0) {
+        for (; j + 1 < nkw; j += 2) {
+          step(F0(), j);
+          step(F1(), j + 1);
+        }
+        if (j < nkw) {
+          step(F0(), j);
+          ++j;
+          pv_tail(pA, B0(), j - 1);  // last block even: its P in pA, its V^T in buffer 0
+        } else {
+          pv_tail(pB, B1(), j - 1);  // last block odd: its P in pB, its V^T in buffer 1
+        }
+      }
+      for (; j < nkb; ++j) {
+        if (j & 1)
+          idle_step(F1(), j);
+        else
+          idle_step(F0(), j);
+      }
     }
+    __builtin_amdgcn_s_waitcnt(0);  // no copy into LDS outlives the block
 
     // epilogue: O = O~ / l (bf16), LSE = (m + log2 l) ln 2
     const int q = qw + r;
