@@ -41,16 +41,20 @@ SETTLE_S = 0.25  # untimed calls before each secondary workload's warm-up
 VALU_OPS_PER_SCORE_D64 = 3.8
 FWD_ROWS_PER_WAVE_D64 = 64  # the d=64 forward's waves own 64 query rows (two 32-row groups)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_causal_b2_h16_n8192_d128_traffic.json")
-FWD_SOURCE = os.path.join(ROOT, "io_aware_softmax_03_amd", "csrc", "fwd_bf16.hip")
+# the sources the forward kernel is compiled from (its file and the shared device header)
+FWD_SOURCES = [os.path.join(ROOT, "io_aware_softmax_03_amd", "csrc", f) for f in ("fwd_bf16.hip", "fa_device.hpp")]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_digest(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_digest(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def time_launches(fn, steps, warmup, settle_s=0.0):
@@ -91,7 +95,7 @@ def traffic_from_profile():
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256_16") != source_digest(FWD_SOURCE):
+    if t.get("source_sha256_16") != source_digest(FWD_SOURCES):
         return None
     return t.get("bytes_per_launch")
 
