@@ -44,7 +44,10 @@ def test_fwd_bf16_gqa(B, N, H, Hkv, d, causal):
     assert max_abs(host(lse), lse_ref) <= TOL_LSE
 
 
-@pytest.mark.parametrize("B,N,H,Hkv,d,causal", [(1, 256, 4, 2, 64, False), (2, 100, 6, 3, 128, True)])
+@pytest.mark.parametrize("B,N,H,Hkv,d,causal", [
+    (1, 256, 4, 2, 64, False), (2, 100, 6, 3, 128, True),
+    (1, 1024, 8, 2, 128, True),   # eight-row query blocks (larger grid) with grouped heads
+])
 def test_fwd_f32_gqa(B, N, H, Hkv, d, causal):
     q, k, v = gen(22, B, N, H, Hkv, d, "f32")
     o, lse = fa().fwd(dev_f32(q), dev_f32(k), dev_f32(v), causal=causal)

@@ -81,6 +81,8 @@ def test_fwd_window_bf16(B, Nq, Nk, H, Hkv, d, causal, left, right):
 @pytest.mark.parametrize("B,Nq,Nk,H,Hkv,d,causal,left,right", [
     (1, 100, 400, 2, 2, 64, True, -1, -1), (1, 300, 300, 2, 1, 128, True, 50, -1),
     (1, 200, 150, 2, 2, 64, True, 20, -1), (1, 128, 128, 2, 2, 128, False, 3, 9),
+    (1, 1000, 2000, 4, 2, 64, True, 300, -1),      # four-row query blocks, several 256-key blocks
+    (1, 2048, 2048, 2, 2, 128, False, 100, 50),    # eight-row query blocks, two-sided window
 ])
 def test_fwd_window_f32(B, Nq, Nk, H, Hkv, d, causal, left, right):
     q, k, v = gen(32, B, Nq, Nk, H, Hkv, d, "f32")
