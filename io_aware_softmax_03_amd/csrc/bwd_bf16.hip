@@ -7,7 +7,9 @@
 // accumulated with atomic additions in device memory).
 //
 // Kernel 1 (preprocess): D_i = sum_c dO_ic O_ic per row, LSE_i * log2(e) (and dK, dV <- 0
-// when key-value heads are shared by groups of query heads).
+// when key-value heads are shared by groups of query heads). Launched only for shared
+// key-value heads; otherwise kernel 3 runs first and forms D and the base-2 LSE of its own
+// queries on the way (from the dO rows it loads anyway), storing them for kernel 2.
 // Kernel 2 (dK, dV): one workgroup per (128-key block, batch*head); each of its 4 waves owns
 // 32 keys and keeps K, V (as MFMA operands) and dK, dV (fp32 accumulators) in registers.
 // It walks 32-query blocks (causal: only those that can see a key of the block); the Q and
@@ -376,7 +378,9 @@ struct DqArgs {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dout;
-  const float* delta;  // D, then the base-2 LSE
+  const uint16_t* o;   // forward output (PRE only)
+  const float* lse;    // natural-log LSE (PRE only)
+  float* delta;        // D, then the base-2 LSE: read, or (PRE) written for kernel 2
   float* dq;
   int heads, kv_heads, group, seqlen, nqb;  // query head h reads key-value head h / group
   int grid;         // workgroups launched
@@ -386,8 +390,10 @@ struct DqArgs {
 
 // Kernel 3: dQ of one 128-query block of one head (one workgroup, 4 waves of 32 queries).
 // About 200 registers per wave, so two workgroups share a CU and one wave's exponentials and
-// LDS reads run beside the other's MFMAs.
-template <int D, bool CAUSAL>
+// LDS reads run beside the other's MFMAs. With PRE (key-value heads not shared) it also does
+// kernel 1's work for its queries: it forms D and the base-2 LSE itself and stores them for
+// kernel 2, which then runs after it, and kernel 1 is not launched.
+template <int D, bool CAUSAL, bool PRE>
 __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(DqArgs p) {
   constexpr int CH = D / 8;
   constexpr int KK = D / 16;
@@ -447,10 +453,43 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(DqArgs p) {
     qf[kk] = __builtin_bit_cast(bf16x8, xq);
     dof[kk] = __builtin_bit_cast(bf16x8, xd);
   }
-  const float* dlt_g = p.delta + ((size_t)b * p.heads + h) * N;
-  const float* lse_g = p.delta + (size_t)p.rows + ((size_t)b * p.heads + h) * N;
-  const float lse2 = myq < N ? lse_g[myq] : 0.f;
-  const float dlt = myq < N ? dlt_g[myq] : 0.f;
+  float* dlt_g = p.delta + ((size_t)b * p.heads + h) * N;
+  float* lse_g = p.delta + (size_t)p.rows + ((size_t)b * p.heads + h) * N;
+  float lse2, dlt;
+  if constexpr (PRE) {
+    // D = sum_c dO_c O_c of this lane's query, added in kernel 1's order, so that both
+    // launch paths give the same bits: a sum of each 8-dim chunk in order, then a binary tree
+    // over the chunks (chunk index 2kk + hh: the lane holds chunks 2kk + hh, the other lane
+    // half the rest, so the tree's first level pairs the two halves)
+    float cs[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 xo = {0u, 0u, 0u, 0u};
+      if (myq < N) xo = *(const u32x4*)(p.o + base + (size_t)myq * rs + 16 * kk + 8 * hh);
+      const u32x4 xd = __builtin_bit_cast(u32x4, dof[kk]);
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = __builtin_fmaf(bf16_lo(xo[e]), bf16_lo(xd[e]), acc);
+        acc = __builtin_fmaf(bf16_hi(xo[e]), bf16_hi(xd[e]), acc);
+      }
+      cs[kk] = pair_sum(acc);
+    }
+#pragma unroll
+    for (int st = 1; st < KK; st <<= 1)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        if ((kk & st) == 0 && (kk & (st - 1)) == 0) cs[kk] = cs[kk] + cs[kk + st];
+    dlt = cs[0];
+    lse2 = myq < N ? p.lse[((size_t)b * p.heads + h) * N + myq] * kLog2e : 0.f;
+    if (hh == 0 && myq < N) {
+      dlt_g[myq] = dlt;
+      lse_g[myq] = lse2;
+    }
+  } else {
+    lse2 = myq < N ? lse_g[myq] : 0.f;
+    dlt = myq < N ? dlt_g[myq] : 0.f;
+  }
 
   f32x16 dq_acc[DB];  // lane holds [query qw + 8i + 4hh + j][dim 32db + r] at [db][4i + j]
 #pragma unroll
@@ -591,25 +630,19 @@ hipError_t launch_main(const MainArgs& m, int blocks, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, bool CAUSAL, bool PRE>
+hipError_t launch_dq(const DqArgs& q, hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, PRE>), dim3((unsigned)q.grid), dim3(kNW * 64), 0, stream, q);
+  return hipGetLastError();
+}
+
+// Without shared key-value heads: kernel 3 (forming D and the base-2 LSE on the way), then
+// kernel 2. With them: kernel 1 (which also clears dK, dV for kernel 2's atomic additions),
+// kernel 2, kernel 3.
 template <int D>
 hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
-  PreArgs pre;
-  pre.o = (const uint16_t*)a.o;
-  pre.dout = (const uint16_t*)a.dout;
-  pre.lse = a.lse;
-  pre.delta = a.delta;
-  pre.dk = a.dk;
-  pre.dv = a.dv;
-  pre.heads = a.heads;
-  pre.seqlen = a.seqlen;
-  pre.rows = (long long)a.batch * a.seqlen * a.heads;
-  pre.rows_kv = a.kv_heads < a.heads ? (long long)a.batch * a.seqlen * a.kv_heads : 0;
-  const long long threads = pre.rows * (D / 8);
-  const long long pblocks = (threads + 255) / 256;
-  if (pblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((bwd_preprocess_kernel<D>), dim3((unsigned)pblocks), dim3(256), 0, stream, pre);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const bool fused = a.kv_heads == a.heads;
+  const long long rows = (long long)a.batch * a.seqlen * a.heads;
 
   MainArgs m;
   m.q = (const uint16_t*)a.q;
@@ -630,15 +663,15 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
   const long long blocks = (long long)m.nkb * a.batch * a.heads;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   m.grid = (int)blocks;
-  m.rows = pre.rows;
-  e = a.causal ? launch_main<D, true>(m, (int)blocks, stream) : launch_main<D, false>(m, (int)blocks, stream);
-  if (e != hipSuccess) return e;
+  m.rows = rows;
 
   DqArgs q;
   q.q = m.q;
   q.k = m.k;
   q.v = m.v;
   q.dout = m.dout;
+  q.o = (const uint16_t*)a.o;
+  q.lse = a.lse;
   q.delta = a.delta;
   q.dq = a.dq;
   q.heads = m.heads;
@@ -646,17 +679,40 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
   q.group = m.group;
   q.seqlen = m.seqlen;
   q.nqb = (a.seqlen + 32 * kNW - 1) / (32 * kNW);
-  q.rows = pre.rows;
+  q.rows = rows;
   q.scale = m.scale;
   q.scale_log2 = m.scale_log2;
   const long long qblocks = (long long)q.nqb * a.batch * a.heads;
   if (qblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   q.grid = (int)qblocks;
-  if (a.causal)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)qblocks), dim3(kNW * 64), 0, stream, q);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)qblocks), dim3(kNW * 64), 0, stream, q);
-  return hipGetLastError();
+
+  hipError_t e;
+  if (fused) {
+    e = a.causal ? launch_dq<D, true, true>(q, stream) : launch_dq<D, false, true>(q, stream);
+    if (e != hipSuccess) return e;
+    return a.causal ? launch_main<D, true>(m, (int)blocks, stream) : launch_main<D, false>(m, (int)blocks, stream);
+  }
+
+  PreArgs pre;
+  pre.o = (const uint16_t*)a.o;
+  pre.dout = (const uint16_t*)a.dout;
+  pre.lse = a.lse;
+  pre.delta = a.delta;
+  pre.dk = a.dk;
+  pre.dv = a.dv;
+  pre.heads = a.heads;
+  pre.seqlen = a.seqlen;
+  pre.rows = rows;
+  pre.rows_kv = (long long)a.batch * a.seqlen * a.kv_heads;
+  const long long threads = pre.rows * (D / 8);
+  const long long pblocks = (threads + 255) / 256;
+  if (pblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((bwd_preprocess_kernel<D>), dim3((unsigned)pblocks), dim3(256), 0, stream, pre);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = a.causal ? launch_main<D, true>(m, (int)blocks, stream) : launch_main<D, false>(m, (int)blocks, stream);
+  if (e != hipSuccess) return e;
+  return a.causal ? launch_dq<D, true, false>(q, stream) : launch_dq<D, false, false>(q, stream);
 }
 
 }  // namespace
