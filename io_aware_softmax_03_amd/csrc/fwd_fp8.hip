@@ -73,10 +73,13 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(QuantArgs p) {
   constexpr int EPT = D / 4;  // elements per thread: each row is spread over 4 threads
   __shared__ float red[4];
   __shared__ __attribute__((aligned(16))) uint8_t tile[VT ? kRows * D : 16];
+  // heads fastest: consecutive workgroups take the same 64 rows of every head, which are
+  // contiguous in the [B, N, H, d] input, so the running workgroups read whole rows
   const int w = group_id_x();
-  const int blk = w % p.nblk;
-  const int bh = w / p.nblk;
-  const int h = bh % p.heads, b = bh / p.heads;
+  const int h = w % p.heads;
+  const int blk = (w / p.heads) % p.nblk;
+  const int b = w / (p.heads * p.nblk);
+  const int bh = b * p.heads + h;
   const int t = thread_id_x();
   const int r = t >> 2, part = t & 3;
   const int row = blk * kRows + r;
