@@ -123,21 +123,17 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(QuantArgs p) {
           y[i] = a + c;
           y[i + hs] = a - c;
         }
+    // (the upper lane of a pair forms o - y, the lower y + o: one FMA with a lane sign of
+    // -1 or +1, exact in the product, so the same single rounding as the difference or sum)
     {
-      const bool upper = (part & 1) != 0;
+      const float sgn = (part & 1) != 0 ? -1.f : 1.f;
 #pragma unroll
-      for (int i = 0; i < EPT; ++i) {
-        const float o = quad_xor<1>(y[i]);
-        y[i] = upper ? o - y[i] : y[i] + o;
-      }
+      for (int i = 0; i < EPT; ++i) y[i] = __builtin_fmaf(y[i], sgn, quad_xor<1>(y[i]));
     }
     {
-      const bool upper = (part & 2) != 0;
+      const float sgn = (part & 2) != 0 ? -1.f : 1.f;
 #pragma unroll
-      for (int i = 0; i < EPT; ++i) {
-        const float o = quad_xor<2>(y[i]);
-        y[i] = upper ? o - y[i] : y[i] + o;
-      }
+      for (int i = 0; i < EPT; ++i) y[i] = __builtin_fmaf(y[i], sgn, quad_xor<2>(y[i]));
     }
 #pragma unroll
     for (int i = 0; i < EPT; ++i) y[i] *= sg[i];
