@@ -202,3 +202,27 @@ def test_bwd_gqa_equals_multi_head_on_repeated_heads_summed():
     assert max_abs(host(dq), host(dq2)) <= 1e-5
     assert max_abs(host(dk), host(dk2.view(B, N, Hkv, grp, d).sum(dim=3))) <= 1e-4
     assert max_abs(host(dv), host(dv2.view(B, N, Hkv, grp, d).sum(dim=3))) <= 1e-4
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_row_terms_identical_on_both_launch_paths(d):
+    """D = rowsum(dO * O) and the base-2 LSE that the backward leaves in its workspace depend
+    on O, dO and the LSE only. The multi-head backward forms them in the dQ kernel, the
+    grouped one in a separate preprocessing launch, in the same order of additions: the
+    two workspaces agree bit for bit (so dS, and dQ, round the same on both paths)."""
+    torch = pytest.importorskip("torch")
+    B, N, H = 2, 333, 4
+    q, k, v = (dev_bf16(x) for x in gen(41, B, N, H, H, d, "bf16"))
+    _, k2, v2 = (dev_bf16(x) for x in gen(42, B, N, H, 2, d, "bf16"))
+    g = dev_bf16(synth.bnhd_tensor(41, synth.TENSOR_DO, B, N, H, d))
+    o, lse = fa().fwd(q, k, v, causal=True)
+    nbytes = fa().lib().fa_bwd_workspace_bytes(B, H, N)
+    rows = B * H * N
+    terms = []
+    for kk, vv in ((k, v), (k2, v2)):
+        ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+        fa().bwd(q, kk, vv, o, lse, g, causal=True, workspace=ws)
+        terms.append(ws.view(torch.int32)[:2 * rows].cpu().numpy())
+    assert np.array_equal(terms[0], terms[1])
+    dref = (host(g).astype(np.float64) * host(o).astype(np.float64)).sum(-1).transpose(0, 2, 1).reshape(-1)
+    assert np.abs(terms[0][:rows].view(np.float32) - dref).max() <= 1e-4 * max(1.0, np.abs(dref).max())
