@@ -18,10 +18,11 @@
 //     from the row-major V tile with the LDS transpose read;
 //   * online softmax in base 2 on scaled scores against a pivot that moves only when a
 //     block's values exceed it by more than a threshold (exact for any shared pivot,
-//     "And on Blackwell"): a wave's first block sets it from its row maximum; after that no
-//     row maximum is taken, P is formed against the current pivot and a lane sum above
-//     kPMax = 2^16 (rare) sends the block through a path that forms its scores again,
-//     moves the pivot to their maximum and rescales O and the sums;
+//     "And on Blackwell"): a wave's first block sets it from its row maximum (plus a headroom
+//     of 16 in log2 units); after that no row maximum is taken, P is formed against the
+//     current pivot and a lane sum above kPMax = 2^16 (rare) sends the block through a path
+//     that forms its scores again, moves the pivot to their maximum (plus the headroom) and
+//     rescales O and the sums;
 //   * key blocks entirely above the causal diagonal are never loaded, and a wave stops at the
 //     last key block its rows can see. The mask is general: query i sees key j when
 //     i + lo_off <= j <= i + hi_off (bottom-right causal for Nq != Nk, sliding windows;
@@ -64,6 +65,13 @@ constexpr float kRescaleThreshold = 8.0f;  // log2 units, for a wave's first blo
 // rows of a causal or windowed sequence) or on large-magnitude scores is often exceeded by 8,
 // and every such block would go through the rescue path.
 constexpr float kPMax = 65536.0f;
+// A pivot is placed this far (log2 units) above the maximum it is taken from (a wave's first
+// block, or a block sent through the rescue path): its P start at most 2^-16, so later scores
+// can pass that maximum by about 16 + 16 before a block needs the rescue path again (the
+// packed workload's Q x 4 heads, whose first blocks of a sequence see few keys, otherwise
+// went through it often). The result is exact for any pivot; weights that matter stay far
+// above the fp32 / bf16 underflow (2^-126).
+constexpr float kPivotHeadroom = 16.0f;
 
 struct FwdKernelArgs {
   const uint16_t* q;
@@ -380,7 +388,7 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64, 2) void fwd_bf16_kernel(FwdKe
       if (wave_any(up)) {
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-          const float m_new = fmaxf(m_ref[g], mt[g]);
+          const float m_new = fmaxf(m_ref[g], mt[g] + kPivotHeadroom);
           const float alpha = exp2_fast(m_ref[g] - m_new);
           m_ref[g] = m_new;
           rescale(g, alpha);
@@ -435,7 +443,7 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64, 2) void fwd_bf16_kernel(FwdKe
             sg[0][i] = (kl > lim || (WINDOW && kl < low)) ? -INFINITY : sg[0][i];
           }
         }
-        const float m_new = fmaxf(m_ref[g], rowmax(sg[0]));
+        const float m_new = fmaxf(m_ref[g], rowmax(sg[0]) + kPivotHeadroom);
         alpha[g] = exp2_fast(m_ref[g] - m_new);
         m_ref[g] = m_new;
         bs[g] = 0.f;

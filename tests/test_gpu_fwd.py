@@ -91,8 +91,10 @@ def test_fwd_bf16_large_scores_rescale():
 @pytest.mark.parametrize("spikes", [
     (4.0, 8.0),     # scores about 90.5 and 181 (130 and 260 base-2 units above the rest):
                     # exp2 against the old pivot overflows fp32
-    (0.5, 1.0),     # about 11.3 and 22.6: the first stays under the kernel's bound on P
-                    # (P in the thousands, no rescue), the second goes past it (no inf)
+    (0.75, 1.5),    # about 17 and 34 (24.5 and 49 base-2 units): against a pivot placed
+                    # 16 units above a first block's maximum (about 6), the first stays under
+                    # the kernel's bound on P (P about 2^3, no rescue), the second goes past
+                    # it (P about 2^27, no inf)
 ])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fwd_bf16_score_spikes_past_overflow(causal, spikes):
