@@ -118,6 +118,25 @@ __device__ __forceinline__ bf16x8 scale_bf16x8(const bf16x8& x, float alpha) {
   return pack_bf16x8(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
 }
 
+// The sequence (of n <= 64) that comes r-th in order of decreasing length, ties by index:
+// lane i ranks sequence i against all others (lengths clamped into the packed tensor as the
+// kernel clamps them), and the lane of rank r names it. Wave-uniform.
+__device__ __forceinline__ int sequence_of_rank(const int* cu, int n, int total, int r) {
+  const int i = thread_id_x() & 63;
+  int len = -1;
+  if (i < n) {
+    const int s = min(max(cu[i], 0), total);
+    len = min(max(cu[i + 1], s), total) - s;
+  }
+  int rank = 0;
+  for (int j = 0; j < n; ++j) {
+    const int lj = __builtin_amdgcn_readlane(len, j);
+    rank += (lj > len || (lj == len && j < i)) ? 1 : 0;
+  }
+  const unsigned long long m = __builtin_amdgcn_ballot_w64(i < n && rank == r);
+  return m ? (int)__builtin_ctzll(m) : r;
+}
+
 template <int D, bool CAUSAL, bool VARLEN, bool WINDOW>
 // (the second bound is the minimum number of waves per SIMD: two, 256 registers each)
 __global__ __launch_bounds__(FwdShape<D>::NW * 64, 2) void fwd_bf16_kernel(FwdKernelArgs p) {
@@ -181,6 +200,11 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64, 2) void fwd_bf16_kernel(FwdKe
   }
   int seq_start, seq_start_k, L, Lk;  // L: query rows
   if constexpr (VARLEN) {
+    // packed batches of up to 64 sequences go longest first: the index decoded above is a
+    // rank in order of decreasing length, so the last workgroups of the launch are those of
+    // the shortest sequences
+    const int nseq = total / (p.nqb * p.heads);
+    if (nseq <= 64) bs = sequence_of_rank(p.cu_seqlens, nseq, p.total_rows, bs);
     // offsets clamped into the packed tensor: a sequence starts in [0, T] and ends in
     // [its start, T], so no access leaves the buffers whatever cu_seqlens holds
     seq_start = min(max(p.cu_seqlens[bs], 0), p.total_rows);
