@@ -210,6 +210,29 @@ def test_varlen_small_full_check(d, causal):
     assert max_abs(lse, lse_ref) <= TOL_LSE_BF16
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_varlen_equal_lengths_each_sequence_once(d):
+    """Sequences are visited longest first, ties by index: repeated lengths (zeros among
+    them) must still map every sequence to exactly one set of workgroups. The output starts
+    as NaN, so a sequence left out or computed twice into the wrong rows would show."""
+    torch = pytest.importorskip("torch")
+    lengths = [300, 0, 300, 47, 0, 300, 47, 600, 1]
+    H = 4
+    cu = synth.cu_seqlens_from_lengths(lengths)
+    q, k, v = (synth.varlen_tensor(9, t, lengths, H, d, "bf16") for t in (synth.TENSOR_Q, synth.TENSOR_K, synth.TENSOR_V))
+    T = sum(lengths)
+    o = torch.full((T, H, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((H, T), float("nan"), dtype=torch.float32, device="cuda")
+    qd, kd, vd, cud = dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_i32(cu)
+    st = fa().lib().fa_fwd_varlen(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                  cud.data_ptr(), len(lengths), T, max(lengths), H, H, d, 1 / math.sqrt(d), 1,
+                                  fa().FA_DTYPE_BF16, torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    o_ref, lse_ref = oracle.attn_fwd_varlen(bits_to_f64(q), bits_to_f64(k), bits_to_f64(v), cu, 1 / math.sqrt(d), True)
+    assert max_abs(host(o), o_ref) <= TOL_O_BF16
+    assert max_abs(host(lse), lse_ref) <= TOL_LSE_BF16
+
+
 def test_varlen_f32():
     lengths = [7, 100, 33]
     cu, q, k, v, o, lse = run_varlen(lengths, 2, 64, True, "f32", 3)
