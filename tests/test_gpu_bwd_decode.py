@@ -124,10 +124,10 @@ def test_decode_split_invariance():
         assert max_abs(host(lse), host(outs[0][1])) <= 1e-5
 
 
-def test_decode_full_size_batch_rows_and_samples():
+def test_decode_full_size_every_element():
     """B=64, H=32, L=32768, d=128 with 64 splits, as the bench runs it. The 34 GB of bf16
-    cache is drawn on the device; every head of batch rows 0 and 63 and sampled (b, h) slices
-    elsewhere are copied back for the oracle (all 2048 slices would copy the whole cache)."""
+    cache is drawn on the device and copied back one batch row at a time (268 MB of K and
+    of V): every head of every batch row against the oracle."""
     torch = pytest.importorskip("torch")
     B, H, L, d = 64, 32, 32768, 128
     gen = torch.Generator(device="cuda")
@@ -137,12 +137,18 @@ def test_decode_full_size_batch_rows_and_samples():
     vc = torch.randn((B, L, H, d), generator=gen, device="cuda", dtype=torch.bfloat16)
     o, lse = fa().decode(q, kc, vc, num_splits=64)
     o, lse = host(o), host(lse)
-    scale = 1 / math.sqrt(d)
-    slices = [(b, h) for b in (0, 63) for h in range(H)] + [(13, 5), (40, 31), (27, 17), (51, 0)]
-    for (b, h) in slices:
-        o_ref, lse_ref = oracle.attn_decode_slice(host(q[b, h]), host(kc[b, :, h]), host(vc[b, :, h]), scale)
-        assert max_abs(o[b, h], o_ref) <= TOL_O, (b, h)
-        assert abs(lse[b, h] - lse_ref) <= TOL_LSE, (b, h)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
+    scale = 1 / math.sqrt(d)
+    qh = host(q)
+    worst_o = worst_l = 0.0
+    for b in range(B):
+        kb, vb = host(kc[b]), host(vc[b])      # [L, H, d]
+        for h in range(H):
+            o_ref, lse_ref = oracle.attn_decode_slice(qh[b, h], kb[:, h], vb[:, h], scale)
+            worst_o = max(worst_o, max_abs(o[b, h], o_ref))
+            worst_l = max(worst_l, abs(lse[b, h] - lse_ref))
+        del kb, vb
+    assert worst_o <= TOL_O, worst_o
+    assert worst_l <= TOL_LSE, worst_l
     del kc, vc
     torch.cuda.empty_cache()
