@@ -6,8 +6,9 @@
 //   * one workgroup per (query block of 256 rows, batch*head), two waves per SIMD: for
 //     d = 128 eight waves of 32 rows (one workgroup per CU), for d = 64 four waves of 64 rows
 //     (two workgroups per CU, each with its own barriers); the query block stays in
-//     registers while 32-key blocks of K and V stream through LDS (double buffered) and are
-//     shared by the workgroup's waves;
+//     registers while 32-key blocks of K and V stream through LDS and are shared by the
+//     workgroup's waves (three buffers each, every copy issued two steps before the step
+//     that reads it, so no step waits for its own copies; two with a sliding window);
 //   * each wave owns whole query rows, so the running max, running sum and output
 //     accumulator of a row never leave the wave (NG = kQW / 32 query groups per wave, each
 //     K or V operand read from LDS feeding NG MFMAs);
@@ -155,16 +156,44 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64, 2) void fwd_bf16_kernel(FwdKe
   constexpr int LOADS = TILE_B / 1024 / CPW;
   static_assert(TILE_B % (1024 * CPW) == 0, "tile must split evenly over the copying waves");
   static_assert(KS == 2, "the score layout below assumes 32-key blocks");
+  // K and V tile buffers each: three (a copy is issued two steps before the step that reads
+  // it, so a step never waits for its own copies), two with a window (waves start at
+  // different blocks, so the three-buffer rotation would need a run-time phase: see the loop)
+  constexpr int NBUF = WINDOW ? 2 : 3;
+  // copies of the current step a wave leaves in flight at the end of a step
+  constexpr int INFLIGHT = NBUF == 3 ? 2 * LOADS : 0;
 
-  // Double-buffered K and V tiles, as four separate LDS objects: every access names its
-  // buffer at compile time, so the compiler can tell a copy into one buffer from reads of
-  // another and does not make those reads wait for the copy.
+  // K and V tiles as separate LDS objects: every access names its buffer at compile time,
+  // so the compiler can tell a copy into one buffer from reads of another and does not make
+  // those reads wait for the copy.
   __shared__ __attribute__((aligned(1024))) char k_lds0[TILE_B];
   __shared__ __attribute__((aligned(1024))) char k_lds1[TILE_B];
+  __shared__ __attribute__((aligned(1024))) char k_lds2[NBUF == 3 ? TILE_B : 16];
   __shared__ __attribute__((aligned(1024))) char v_lds0[TILE_B];
   __shared__ __attribute__((aligned(1024))) char v_lds1[TILE_B];
-  auto kbuf = [&](auto bc) -> char* { return (decltype(bc)::value & 1) ? k_lds1 : k_lds0; };
-  auto vbuf = [&](auto bc) -> char* { return (decltype(bc)::value & 1) ? v_lds1 : v_lds0; };
+  __shared__ __attribute__((aligned(1024))) char v_lds2[NBUF == 3 ? TILE_B : 16];
+  auto kbuf = [&](auto bc) -> char* {
+    constexpr int b = decltype(bc)::value % NBUF;
+    return b == 0 ? k_lds0 : (b == 1 ? k_lds1 : k_lds2);
+  };
+  auto vbuf = [&](auto bc) -> char* {
+    constexpr int b = decltype(bc)::value % NBUF;
+    return b == 0 ? v_lds0 : (b == 1 ? v_lds1 : v_lds2);
+  };
+  // Workgroup barrier once this wave's copies other than the INFLIGHT most recent ones have
+  // landed (and, with LGKM, its LDS stores). __syncthreads() would wait for every copy: its
+  // workgroup-scope release fence waits for all outstanding copies into LDS. The
+  // wavefront-scope fences emit nothing; they keep the compiler from moving memory accesses
+  // across the barrier.
+  auto sync_copies = [](auto lgkmc) {
+    constexpr int lgkm = decltype(lgkmc)::value ? 0 : 0xF00;  // lgkmcnt(0), or no LGKM wait
+    __builtin_amdgcn_s_waitcnt(0x70 | lgkm | INFLIGHT);      // vmcnt(INFLIGHT), no EXP wait
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  using LgkmToo = std::integral_constant<bool, true>;
+  using VmOnly = std::integral_constant<bool, false>;
 
   // ---- work decode, XCD-aware: workgroup w runs on XCD w % 8. With a key-value head count
   // divisible by 8, XCD x takes key-value heads x, x+8, ... of every sequence with every query
@@ -521,16 +550,22 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64, 2) void fwd_bf16_kernel(FwdKe
     using KT = std::integral_constant<bool, true>;
     using VT = std::integral_constant<bool, false>;
 
-    // ---- prologue: K(0) -> K buffer 0, K(1) -> K buffer 1; V buffer 1 is cleared so the
-    // first step's P V (a zero P block times that buffer) adds exact zeros. A block whose
-    // rows see no key at all skips to the epilogue (zeros, LSE -inf).
+    // ---- prologue: K(0) .. K(NBUF-1) -> K buffers 0 .. NBUF-1 (and with three buffers
+    // V(0) -> V buffer 0, issued last); V buffer NBUF-1 is cleared so the first step's P V (a
+    // zero P block times that buffer) adds exact zeros. A block whose rows see no key at all
+    // skips to the epilogue (zeros, LSE -inf).
     if (ntiles > 0) {
     issue(KT(), B0(), 0);
     issue(KT(), B1(), min(1, ntiles - 1));
+    if constexpr (NBUF == 3) {
+      issue(KT(), std::integral_constant<int, 2>(), min(2, ntiles - 1));
+      issue(VT(), B0(), 0);
+    }
     {
+      char* vz = vbuf(std::integral_constant<int, NBUF - 1>());
       u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int o = tid * 16; o < TILE_B; o += kNW * 64 * 16) *(u32x4*)(v_lds1 + o) = z;
+      for (int o = tid * 16; o < TILE_B; o += kNW * 64 * 16) *(u32x4*)(vz + o) = z;
     }
     f32x16 sA[NG], sB[NG];
     bf16x8 pA[NG][KS], pB[NG][KS];
@@ -538,8 +573,7 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64, 2) void fwd_bf16_kernel(FwdKe
     for (int g = 0; g < NG; ++g)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) pB[g][ks] = bf16x8{};
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    sync_copies(LgkmToo());  // K(0), K(1) and the cleared buffer are in place
     if (ws == 0 && wtiles > 0) {
       qk(sA, B0());
 #pragma unroll
@@ -550,12 +584,17 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64, 2) void fwd_bf16_kernel(FwdKe
       for (int g = 0; g < NG; ++g) mt[g] = rowmax(sA[g]);
       repivot(mt, pB);
     }
-    __syncthreads();  // every wave is done with K(0)
+    sync_copies(VmOnly());  // every wave is done with K(0)
 
-    // ---- step j (parity PH = j & 1), for j < wtiles: loads K(j+2) -> K buffer j&1 and
-    // V(j) -> V buffer j&1; computes S(j+1) = K(j+1) Q^T from K buffer !(j&1), P(j) from S(j),
-    // and O += V(j-1) P(j-1) from V buffer !(j&1). Past the last block the loads repeat the
-    // last block (its buffer is free and the copy is never read), so a step has no branches.
+    // ---- step j (phase PH = j % 6 with three buffers, j % 2 with two; tile t lives in
+    // buffer t % NBUF), for j < wtiles:
+    // computes S(j+1) = K(j+1) Q^T, P(j) from S(j), and O += V(j-1) P(j-1); copies
+    // K(j+NBUF) and V(j+NBUF-2) (into the buffers of K(j) and V(j-2), which every wave has
+    // finished with by the previous step's barrier), so a copy lands within the step after
+    // the one that issues it, two steps before it is read with three buffers; ends by waiting
+    // for the copies of the step before (with two buffers: of this step) and a barrier. Past
+    // the last block the loads repeat the last block (its buffer is free and the copy is
+    // never read), so a step has no branches.
     //
     // The step is laid out by hand as NSLOT slots, one MFMA each (the score MFMAs first, then
     // those of P V), fenced by scheduling barriers. Each slot also carries a fixed share of
@@ -587,6 +626,13 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64, 2) void fwd_bf16_kernel(FwdKe
       return t < -1 ? -1 : t;
     };
 
+    // the copies of step j: K(j+NBUF) -> the buffer of K(j), V(j+NBUF-2) -> that of V(j-2)
+    auto issue_step = [&](auto phase, int j) {
+      constexpr int PH = decltype(phase)::value;
+      issue(KT(), std::integral_constant<int, PH>(), min(j + NBUF, ntiles - 1));
+      issue(VT(), std::integral_constant<int, PH + NBUF - 2>(), min(j + NBUF - 2, ntiles - 1));
+    };
+
     auto step = [&](auto phase, int j) {
       constexpr int PH = decltype(phase)::value;
       constexpr bool ODD = PH & 1;
@@ -594,8 +640,8 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64, 2) void fwd_bf16_kernel(FwdKe
       f32x16(&n)[NG] = ODD ? sA : sB;       // S(j+1)
       bf16x8(&pc)[NG][KS] = ODD ? pB : pA;  // P(j)
       bf16x8(&pp)[NG][KS] = ODD ? pA : pB;  // P(j-1)
-      const char* kb = kbuf(std::integral_constant<int, PH + 1>());  // K(j+1)
-      const char* vb = vbuf(std::integral_constant<int, PH + 1>());  // V(j-1)
+      const char* kb = kbuf(std::integral_constant<int, PH + 1>());         // K(j+1)
+      const char* vb = vbuf(std::integral_constant<int, PH + NBUF - 1>());  // V(j-1)
       float mneg[NG];
 #pragma unroll
       for (int g = 0; g < NG; ++g) mneg[g] = -m_ref[g];
@@ -654,8 +700,7 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64, 2) void fwd_bf16_kernel(FwdKe
       // preamble (slot -1): the first LDS reads, the row-sum MFMAs and the first FMAs; then
       // this step's copies into LDS (their scalar set-up runs while the reads are in flight)
       slot(std::integral_constant<int, -1>());
-      issue(KT(), std::integral_constant<int, PH>(), min(j + 2, ntiles - 1));
-      issue(VT(), std::integral_constant<int, PH>(), j);
+      issue_step(phase, j);
       __builtin_amdgcn_sched_barrier(0);
       static_for<0, NSLOT + 1>(slot);
       // tail: this lane's sums of P(j), the bf16 operands of P(j)
@@ -692,26 +737,21 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64, 2) void fwd_bf16_kernel(FwdKe
       }
 #pragma unroll
       for (int g = 0; g < NG; ++g) l_part[g] += bs[g];
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of K(j+2), V(j) have landed
-      __syncthreads();
+      sync_copies(VmOnly());  // the copies of K(j+2), V(j) have landed
     };
     // a step of a wave past its last key block: its share of the loads, and the barrier
     auto idle_step = [&](auto phase, int j) {
-      constexpr int PH = decltype(phase)::value;
-      issue(KT(), std::integral_constant<int, PH>(), min(j + 2, ntiles - 1));
-      issue(VT(), std::integral_constant<int, PH>(), j);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      issue_step(phase, j);
+      sync_copies(VmOnly());
     };
-    // step j - 1 of a wave whose first block is j (window): that step's loads, then S(j)
-    // from K buffer j&1, formed as the prologue forms S(0); P(j-1) is zero
+    // step j of a wave whose first block is j + 1 (window): that step's loads, then S(j+1),
+    // formed as the prologue forms S(0); P(j) is zero
     auto pre_step = [&](auto phase, int j) {
       constexpr int PH = decltype(phase)::value;
       constexpr bool ODD = PH & 1;
       f32x16(&n)[NG] = ODD ? sA : sB;       // S(j+1), where step j+1 reads it
       bf16x8(&pz)[NG][KS] = ODD ? pB : pA;  // P(j), step j+1's previous block
-      issue(KT(), std::integral_constant<int, PH>(), min(j + 2, ntiles - 1));
-      issue(VT(), std::integral_constant<int, PH>(), j);
+      issue_step(phase, j);
 #pragma unroll
       for (int g = 0; g < NG; ++g)
 #pragma unroll
@@ -724,52 +764,108 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64, 2) void fwd_bf16_kernel(FwdKe
 #pragma unroll
       for (int g = 0; g < NG; ++g) mt[g] = rowmax(n[g]);
       repivot(mt, pz);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      sync_copies(VmOnly());
     };
-    using F0 = std::integral_constant<int, 0>;
-    using F1 = std::integral_constant<int, 1>;
     // Every wave runs ntiles steps (the same barriers); it computes blocks ws .. wtiles-1,
-    // and the last P block of the wave is multiplied into O right after them.
+    // and the last P block of the wave is multiplied into O right after them. The main loop
+    // runs a whole period of phases a pass (6 steps with three buffers, 2 with two); steps
+    // whose phase is known only at run time (idle steps, the tail) dispatch on it. (A window wave may start at any block:
+    // with three buffers its first steps would need such a dispatch inside the loop, which
+    // made the compiler spill; windows keep two buffers and the two-step loop.)
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
     int j = 0;
     const bool computes = wtiles > ws;
-    if constexpr (WINDOW) {
-      if (computes && ws > 0) {
-        for (; j + 1 < ws; ++j) {
+    if constexpr (NBUF == 2) {
+      if constexpr (WINDOW) {
+        if (computes && ws > 0) {
+          for (; j + 1 < ws; ++j) {
+            if (j & 1)
+              idle_step(P1(), j);
+            else
+              idle_step(P0(), j);
+          }
           if (j & 1)
-            idle_step(F1(), j);
+            pre_step(P1(), j);
           else
-            idle_step(F0(), j);
-        }
-        if (j & 1)
-          pre_step(F1(), j);
-        else
-          pre_step(F0(), j);
-        ++j;
-        if (j & 1) {  // keep the pairs below starting on an even block
-          step(F1(), j);
+            pre_step(P0(), j);
           ++j;
+          if (j & 1) {  // keep the pairs below starting on an even block
+            step(P1(), j);
+            ++j;
+          }
         }
       }
-    }
-    if (computes) {
-      for (; j + 1 < wtiles; j += 2) {
-        step(F0(), j);
-        step(F1(), j + 1);
+      if (computes) {
+        for (; j + 1 < wtiles; j += 2) {
+          step(P0(), j);
+          step(P1(), j + 1);
+        }
+        if (j < wtiles) {
+          step(P0(), j);
+          ++j;
+          pv_tail(pA, P0());  // last block even: its P is in pA, its V in buffer 0
+        } else {
+          pv_tail(pB, P1());  // last block odd: its P is in pB, its V in buffer 1
+        }
       }
-      if (j < wtiles) {
-        step(F0(), j);
-        ++j;
-        pv_tail(pA, B0());  // last block even: its P is in pA, its V in buffer 0
-      } else {
-        pv_tail(pB, B1());  // last block odd: its P is in pB, its V in buffer 1
+      for (; j < ntiles; ++j) {
+        if (j & 1)
+          idle_step(P1(), j);
+        else
+          idle_step(P0(), j);
       }
-    }
-    for (; j < ntiles; ++j) {
-      if (j & 1)
-        idle_step(F1(), j);
-      else
-        idle_step(F0(), j);
+    } else {
+      using P2 = std::integral_constant<int, 2>;
+      using P3 = std::integral_constant<int, 3>;
+      using P4 = std::integral_constant<int, 4>;
+      using P5 = std::integral_constant<int, 5>;
+      if (computes) {
+        for (; j + 5 < wtiles; j += 6) {
+          step(P0(), j);
+          step(P1(), j + 1);
+          step(P2(), j + 2);
+          step(P3(), j + 3);
+          step(P4(), j + 4);
+          step(P5(), j + 5);
+        }
+        if (j < wtiles) {
+          step(P0(), j);
+          if (++j < wtiles) {
+            step(P1(), j);
+            if (++j < wtiles) {
+              step(P2(), j);
+              if (++j < wtiles) {
+                step(P3(), j);
+                if (++j < wtiles) {
+                  step(P4(), j);
+                  ++j;
+                }
+              }
+            }
+          }
+        }
+        // the last block wtiles-1: its P is in pA (even) or pB (odd), its V in buffer
+        // (wtiles-1) % 3
+        switch ((wtiles - 1) % 6) {
+          case 0: pv_tail(pA, P0()); break;
+          case 1: pv_tail(pB, P1()); break;
+          case 2: pv_tail(pA, P2()); break;
+          case 3: pv_tail(pB, P3()); break;
+          case 4: pv_tail(pA, P4()); break;
+          default: pv_tail(pB, P5()); break;
+        }
+      }
+      for (; j < ntiles; ++j) {
+        switch (j % 6) {
+          case 0: idle_step(P0(), j); break;
+          case 1: idle_step(P1(), j); break;
+          case 2: idle_step(P2(), j); break;
+          case 3: idle_step(P3(), j); break;
+          case 4: idle_step(P4(), j); break;
+          default: idle_step(P5(), j); break;
+        }
+      }
     }
     }  // ntiles > 0
 
