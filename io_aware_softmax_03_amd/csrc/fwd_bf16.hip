@@ -694,6 +694,17 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64, 2) void fwd_bf16_kernel(FwdKe
 #pragma unroll
         for (int k = 0; k < NG * KS; ++k)
           if (lsum_slot(k) == t) lsum[k / KS] = mfma16(sel, pp[k / KS][k % KS], lsum[k / KS]);
+        // d = 128: issue priority falls in four stages as a wave moves through its step, so
+        // that of the two waves of a SIMD (one workgroup) the one behind is issued first (the
+        // older wave otherwise wins every tie, runs ahead and waits at the barrier while the
+        // younger one issues alone). At d = 64 the two waves of a SIMD belong to different
+        // workgroups and the stages made no difference.
+        if constexpr (D == 128) {
+          if constexpr (t == -1) __builtin_amdgcn_s_setprio(3);
+          if constexpr (t == NSLOT / 4) __builtin_amdgcn_s_setprio(2);
+          if constexpr (t == NSLOT / 2) __builtin_amdgcn_s_setprio(1);
+          if constexpr (t == 3 * NSLOT / 4) __builtin_amdgcn_s_setprio(0);
+        }
         __builtin_amdgcn_sched_barrier(0);
       };
 
