@@ -33,8 +33,9 @@ FLAGS = [
 # score tiles in AGPRs and cost a copy to VGPRs for each softmax step. With the VGPR form the
 # output accumulators and scores sit in VGPRs and the Q operands in AGPRs.
 # The FP8 forward kernel needs the same form to stay out of scratch memory. In the backward
-# kernel the AGPR form copied every score, dP and dQ tile between the register files each
-# step.
+# kernels the AGPR form copied every score, dP and dQ tile between the register files each
+# step; there the dK, dV accumulators (the dK/dV kernel runs one wave per SIMD) are put in
+# AGPRs by their own inline-assembly MFMAs instead.
 FILE_FLAGS = {
     "fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "fwd_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],

@@ -115,6 +115,17 @@ template <int D>
 __device__ __forceinline__ int swz_row(int row) {
   return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
 }
+// c += a b on the matrix core with the accumulator in AGPRs. The file's MFMAs otherwise get
+// VGPR accumulators (the scores and dP are read by the VALU); dK and dV would then take 128
+// of the 256 VGPRs, and the kernel spilled to AGPRs and recomputed LDS addresses in its loop.
+// The accumulator is written and read only by this chain (back-to-back accumulation into the
+// same registers needs no wait states) until the guard before the epilogue; its A and B
+// operands come from VGPRs written by the VALU or by LDS reads, which the compiler waits for
+// as for any register input of inline assembly.
+__device__ __forceinline__ void mfma32_agpr(f32x16& c, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
   constexpr int CH = D / 8;
@@ -227,6 +238,25 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
     asm volatile("s_barrier" ::: "memory");
   };
 
+  // Per-lane byte offsets of the LDS operand reads within a Q or dO tile, the same for every
+  // tile and buffer: computed once (recomputed in the loop, they cost more VALU instructions
+  // per step than the products' softmax work). Row reads (A operands of S = Q K^T and
+  // dP = dO V^T): row r, chunk 2kk + hh. Transposing reads (B operands of dV += P^T dO and
+  // dK += dS^T Q): k-step ks, 32-dim block db, rows 16ks + 4hh + gi/4 and 8 further.
+  constexpr int NPT = 2 * DB;
+  int rw_off[KK], tr_a[NPT], tr_b[NPT];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) rw_off[kk] = (r * D + (((2 * kk + hh) ^ swz_row<D>(r)) << 3)) * 2;
+#pragma unroll
+  for (int t = 0; t < NPT; ++t) {
+    const int ks = t / DB, db = t % DB;
+    const int row_a = 16 * ks + 4 * hh + (gi >> 2);
+    const int row_b = row_a + 8;
+    const int col = db * 32 + 16 * nh + 4 * (gi & 3);
+    tr_a[t] = (row_a * D + (((col >> 3) ^ swz_row<D>(row_a)) << 3) + (col & 7)) * 2;
+    tr_b[t] = (row_b * D + (((col >> 3) ^ swz_row<D>(row_b)) << 3) + (col & 7)) * 2;
+  }
+
   // prologue: tile 0, its LSE and D
   if (nsteps > 0) issue_tile(std::integral_constant<int, 0>(), 0);
   __builtin_amdgcn_s_waitcnt(0);
@@ -254,9 +284,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
       // Q and dO operands of k-step kk are read two k-steps ahead of their MFMAs
       bf16x8 aq[KK], ad[KK];
       auto rd = [&](int kk) {
-        const int c = 2 * kk + hh;
-        aq[kk] = __builtin_bit_cast(bf16x8, *(const u32x4*)(sq + r * D + ((c ^ swz_row<D>(r)) << 3)));
-        ad[kk] = __builtin_bit_cast(bf16x8, *(const u32x4*)(sd + r * D + ((c ^ swz_row<D>(r)) << 3)));
+        aq[kk] = __builtin_bit_cast(bf16x8, *(const u32x4*)((const char*)sq + rw_off[kk]));
+        ad[kk] = __builtin_bit_cast(bf16x8, *(const u32x4*)((const char*)sd + rw_off[kk]));
       };
       rd(0);
       rd(1);
@@ -302,14 +331,10 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
       constexpr int NP = 2 * DB;
       bf16x8 bdo[NP], bq[NP];
       auto rd = [&](int t) {
-        const int ks = t / DB, db = t % DB;
-        const int row_a = 16 * ks + 4 * hh + (gi >> 2);
-        const int row_b = row_a + 8;
-        const int col = db * 32 + 16 * nh + 4 * (gi & 3);
-        const int ca = (((col >> 3) ^ swz_row<D>(row_a)) << 3) + (col & 7);
-        const int cb = (((col >> 3) ^ swz_row<D>(row_b)) << 3) + (col & 7);
-        bdo[t] = join_tr(lds_read_tr(sd + row_a * D + ca), lds_read_tr(sd + row_b * D + cb));
-        bq[t] = join_tr(lds_read_tr(sq + row_a * D + ca), lds_read_tr(sq + row_b * D + cb));
+        const char* cd = (const char*)sd;
+        const char* cq = (const char*)sq;
+        bdo[t] = join_tr(lds_read_tr((const uint16_t*)(cd + tr_a[t])), lds_read_tr((const uint16_t*)(cd + tr_b[t])));
+        bq[t] = join_tr(lds_read_tr((const uint16_t*)(cq + tr_a[t])), lds_read_tr((const uint16_t*)(cq + tr_b[t])));
       };
       bf16x8 ap0, as0, ap1, as1;
 #pragma unroll
@@ -320,8 +345,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        dv_acc[db] = mfma32(ap0, bdo[db], dv_acc[db]);
-        dk_acc[db] = mfma32(as0, bq[db], dk_acc[db]);
+        mfma32_agpr(dv_acc[db], ap0, bdo[db]);
+        mfma32_agpr(dk_acc[db], as0, bq[db]);
         rd(DB + db);
 #pragma unroll
         for (int i = 8 + db * (8 / DB); i < 8 + (db + 1) * (8 / DB); ++i) {
@@ -334,8 +359,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
       pack_ks(1, ap1, as1);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        dv_acc[db] = mfma32(ap1, bdo[DB + db], dv_acc[db]);
-        dk_acc[db] = mfma32(as1, bq[DB + db], dk_acc[db]);
+        mfma32_agpr(dv_acc[db], ap1, bdo[DB + db]);
+        mfma32_agpr(dk_acc[db], as1, bq[DB + db]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -350,6 +375,13 @@ __global__ __launch_bounds__(kNW * 64, 1) void bwd_main_kernel(MainArgs p) {
     step(std::integral_constant<int, 0>(), st);
     ++st;
   }
+
+  // The last products' results are read only after enough wait states (the compiler cannot
+  // count them for an MFMA issued from inline assembly): 24 NOP cycles, with the
+  // accumulators as operands so that no read of them moves above.
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(dv_acc[db]), "+a"(dk_acc[db]));
 
   // dK = scale * dS^T Q, dV = P^T dO; lane holds [key 8i + 4hh + j][dim db*32 + r]. A key-value
   // head shared by a group of query heads sums the group's contributions (added into the
@@ -389,7 +421,7 @@ struct DqArgs {
 };
 
 // Kernel 3: dQ of one 128-query block of one head (one workgroup, 4 waves of 32 queries).
-// About 200 registers per wave, so two workgroups share a CU and one wave's exponentials and
+// 216 registers per wave, so two workgroups share a CU and one wave's exponentials and
 // LDS reads run beside the other's MFMAs. With PRE (key-value heads not shared) it also does
 // kernel 1's work for its queries: it forms D and the base-2 LSE itself and stores them for
 // kernel 2, which then runs after it, and kernel 1 is not launched.
@@ -525,6 +557,24 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(DqArgs p) {
     }
   };
 
+  // Per-lane byte offsets of the LDS operand reads within a K or V tile, computed once (as in
+  // kernel 2). Row reads (A operands of S^T = K Q^T, dP^T = V dO^T): row r, chunk 2kk + hh.
+  // Transposing reads of K (B operand of dQ += dS K): k-step ks, 32-dim block db, rows
+  // 16ks + 4hh + gi/4 and 8 further.
+  constexpr int NPT = 2 * DB;
+  int rw_off[KK], tr_a[NPT], tr_b[NPT];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) rw_off[kk] = (r * D + (((2 * kk + hh) ^ swz_row<D>(r)) << 3)) * 2;
+#pragma unroll
+  for (int t = 0; t < NPT; ++t) {
+    const int ks = t / DB, db = t % DB;
+    const int row_a = 16 * ks + 4 * hh + (gi >> 2);
+    const int row_b = row_a + 8;
+    const int col = db * 32 + 16 * nh + 4 * (gi & 3);
+    tr_a[t] = (row_a * D + (((col >> 3) ^ swz_row<D>(row_a)) << 3) + (col & 7)) * 2;
+    tr_b[t] = (row_b * D + (((col >> 3) ^ swz_row<D>(row_b)) << 3) + (col & 7)) * 2;
+  }
+
   if (ntiles > 0) issue_tile(std::integral_constant<int, 0>(), 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -541,9 +591,8 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(DqArgs p) {
         // K and V operands of k-step kk read two k-steps ahead of their MFMAs
         bf16x8 ak[KK], av[KK];
         auto rd = [&](int kk) {
-          const int c = 2 * kk + hh;
-          ak[kk] = __builtin_bit_cast(bf16x8, *(const u32x4*)(sk + r * D + ((c ^ swz_row<D>(r)) << 3)));
-          av[kk] = __builtin_bit_cast(bf16x8, *(const u32x4*)(sv + r * D + ((c ^ swz_row<D>(r)) << 3)));
+          ak[kk] = __builtin_bit_cast(bf16x8, *(const u32x4*)((const char*)sk + rw_off[kk]));
+          av[kk] = __builtin_bit_cast(bf16x8, *(const u32x4*)((const char*)sv + rw_off[kk]));
         };
         rd(0);
         rd(1);
@@ -587,13 +636,8 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(DqArgs p) {
       constexpr int NP = 2 * DB;
       bf16x8 bk[NP];
       auto rdk = [&](int t) {
-        const int ks = t / DB, db = t % DB;
-        const int row_a = 16 * ks + 4 * hh + (gi >> 2);
-        const int row_b = row_a + 8;
-        const int col = db * 32 + 16 * nh + 4 * (gi & 3);
-        const int ca = (((col >> 3) ^ swz_row<D>(row_a)) << 3) + (col & 7);
-        const int cb = (((col >> 3) ^ swz_row<D>(row_b)) << 3) + (col & 7);
-        bk[t] = join_tr(lds_read_tr(sk + row_a * D + ca), lds_read_tr(sk + row_b * D + cb));
+        const char* ck = (const char*)sk;
+        bk[t] = join_tr(lds_read_tr((const uint16_t*)(ck + tr_a[t])), lds_read_tr((const uint16_t*)(ck + tr_b[t])));
       };
       rdk(0);
       rdk(1);
