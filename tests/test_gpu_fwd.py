@@ -75,6 +75,21 @@ def test_fwd_bf16(B, N, H, d, causal):
     assert max_abs(host(lse), lse_ref) <= TOL_LSE_BF16
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [33, 80, 100, 150, 192, 224, 250])
+def test_fwd_bf16_few_key_blocks(N, causal, d):
+    """One query block over 2 to 8 key blocks of 32: the key loop runs a whole pass of six
+    steps or none, then a tail of up to five steps, and the last block's P V is taken from
+    each of the six step phases (its buffer and P registers). The prologue's copies past the
+    last block repeat it."""
+    qb, kb, vb = gen_dense(11, 1, N, 2, d, "bf16")
+    o, lse = fa().fwd(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), causal=causal)
+    o_ref, lse_ref = oracle.attn_fwd(bits_to_f64(qb), bits_to_f64(kb), bits_to_f64(vb), 1 / math.sqrt(d), causal)
+    assert max_abs(host(o), o_ref) <= TOL_O_BF16
+    assert max_abs(host(lse), lse_ref) <= TOL_LSE_BF16
+
+
 def test_fwd_bf16_large_scores_rescale():
     """Scores of tens of units force the running maximum (and the rescale) to move often."""
     B, N, H, d = 1, 777, 2, 128
