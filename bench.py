@@ -14,6 +14,12 @@ the packed varlen
 forward (16 sequences, H=32, d=64) and the fp32 forward (N=256, d=64); and the float64
 CPU oracle timed on a bounded sample of the headline workload (field "cpu_baseline").
 
+Every workload, the headline included, first runs its call untimed for about SETTLE_S seconds
+(field "settle_s"; --settle-s), then its W warm-up calls, then the K timed ones: after a
+switch between workloads the clock takes a fraction of a second to settle (the headline
+measured right after the paged decode with W=5, K=20 ran 7% slower than after 1500 warm-up
+calls; with the settle, within 1.5%).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -34,7 +40,7 @@ METRIC = "attention fwd TFLOP/s (bf16 causal N=8192 d=128) and % of MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
 PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS  # dense e4m3 matrix-core peak (5.0 PFLOP/s)
-SETTLE_S = 0.25  # untimed calls before each secondary workload's warm-up
+SETTLE_S = 0.25  # seconds of untimed calls before each workload's warm-up
 # other (non-transcendental) VALU lane-operations per formed score of the d=64 packed forward,
 # from its SQ counters (SQ_INSTS_VALU - SQ_INSTS_VALU_TRANS_F32 per formed score x 64 lanes;
 # profiles/fwd_bwd_counters.md)
@@ -345,7 +351,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--settle-s", type=float, default=SETTLE_S,
-                    help="untimed seconds of calls before each secondary workload (0 for profiler runs)")
+                    help="untimed seconds of calls before each workload's warm-up, the headline's too "
+                         "(0 for profiler runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (untimed), so that a counter "
                          "profile of this command holds a kernel of known traffic to scale HBM counters by")
@@ -369,9 +376,9 @@ def main():
         log(f"[bench] calibration copy: {n} bytes read, {n} bytes written")
         del src, dst
 
-    # The secondary workloads run first (each after a short untimed settle of its own), so the
-    # headline's W warm-up steps and K timed steps follow sustained GPU load rather than an
-    # idle GPU whose clock is still rising.
+    # The secondary workloads run first, so the headline follows sustained GPU load rather than
+    # an idle GPU whose clock is still rising; like each of them it then runs untimed for
+    # SETTLE_S seconds before its W warm-up steps and K timed steps.
     extra = None
     if not args.no_extra:
         log("[bench] secondary workloads")
@@ -388,7 +395,7 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     step = lambda: fa.fwd(q, k, v, causal=True, out=(o, lse))  # noqa: E731
-    wall_ms, kern_ms, kern_min = time_launches(step, args.steps, args.warmup)
+    wall_ms, kern_ms, kern_min = time_launches(step, args.steps, args.warmup, SETTLE_S)
     kern_median = time_launches.last_median
     flops = costs.fwd_flops(B, H, N, d, True)
     value = flops / (wall_ms * 1e-3) / 1e12
@@ -404,6 +411,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": SETTLE_S,
         "ms_per_step": round(wall_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
