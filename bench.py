@@ -216,7 +216,7 @@ def extra_measurements(steps, only=None):
 
     def _fp8():
         # FP8 forward on the headline shape (causal B=2 H=16 N=8192 d=128), Q and K rotated:
-        # three quantization launches plus the attention launch per call
+        # one quantization launch (Q, K, V) plus the attention launch per call
         B, H, N, d = 2, 16, 8192, 128
         gen.manual_seed(11)
         q, k, v = (torch.randn((B, N, H, d), generator=gen, device="cuda", dtype=torch.bfloat16) for _ in range(3))

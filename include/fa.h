@@ -196,8 +196,8 @@ size_t fa_fwd_fp8_workspace_bytes(int B, int H, int Hkv, int N, int d);
  *              32*((s>>4)&1) + 8*((s>>2)&3) + 4*(s>>5) + (s&3) of the block, then int32
  *              exponents [B, H, nb], [B, Hkv, nb], [B, Hkv, nb]: a block's values are
  *              its e4m3 codes (OCP, bias 7) times 2^exponent.
- * Causal is top-left (square). The call enqueues three quantization launches and the
- * attention launch.
+ * Causal is top-left (square). The call enqueues one quantization launch (Q, K and V) and
+ * the attention launch.
  */
 int fa_fwd_fp8(const void* q, const void* k, const void* v, const float* signs, void* o, float* lse,
                int B, int H, int Hkv, int N, int d, float scale, int causal,

@@ -2,8 +2,8 @@
 //
 // Two kernels after one another on the caller's stream:
 //
-// 1. fp8_quant_kernel, once each for Q, K and V: one workgroup per block of 64 rows of one
-//    head. Q and K rows are optionally rotated by R = H_d D / sqrt(d) (incoherent
+// 1. fp8_quant_qkv_kernel, one launch for Q, K and V (their workgroups interleaved): one
+//    workgroup per block of 64 rows of one head. Q and K rows are optionally rotated by R = H_d D / sqrt(d) (incoherent
 //    processing: Hadamard matrix times a random +-1 diagonal). The kernel forms x H_d D with
 //    the fast Walsh-Hadamard transform in fp32 (butterflies at strides 1, 2, ..., d/2) and
 //    leaves the 1/sqrt(d) to the score scale (1/d there). Each block gets one power-of-two
@@ -69,13 +69,12 @@ __device__ __forceinline__ float quad_xor(float x) {
 }
 
 template <int D, bool ROTATE, bool VT>
-__global__ __launch_bounds__(256) void fp8_quant_kernel(QuantArgs p) {
+__device__ __forceinline__ void fp8_quant_block(const QuantArgs& p, int w) {
   constexpr int EPT = D / 4;  // elements per thread: each row is spread over 4 threads
   __shared__ float red[4];
   __shared__ __attribute__((aligned(16))) uint8_t tile[VT ? kRows * D : 16];
-  // heads fastest: consecutive workgroups take the same 64 rows of every head, which are
+  // heads fastest: consecutive blocks w take the same 64 rows of every head, which are
   // contiguous in the [B, N, H, d] input, so the running workgroups read whole rows
-  const int w = group_id_x();
   const int h = w % p.heads;
   const int blk = (w / p.heads) % p.nblk;
   const int b = w / (p.heads * p.nblk);
@@ -198,6 +197,26 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(QuantArgs p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) *(uint32_t*)(dst + (4 * dg + e) * kRows + 4 * sg) = od[e];
     }
+  }
+}
+
+// Q, K (rotated when ROTATE) and V (transposed) quantized by one launch: workgroups
+// 3i, 3i+1, 3i+2 take block i of Q, K and V (i < nkv), the rest the remaining blocks of Q
+// (more query than key-value heads), so the three passes' loads, arithmetic and stores overlap
+// and there is one tail instead of three.
+template <int D, bool ROTATE>
+__global__ __launch_bounds__(256) void fp8_quant_qkv_kernel(QuantArgs q, QuantArgs k, QuantArgs v, int nkv) {
+  const int w = group_id_x();
+  if (w < 3 * nkv) {
+    const int t = w % 3, i = w / 3;
+    if (t == 0)
+      fp8_quant_block<D, ROTATE, false>(q, i);
+    else if (t == 1)
+      fp8_quant_block<D, ROTATE, false>(k, i);
+    else
+      fp8_quant_block<D, false, true>(v, i);
+  } else {
+    fp8_quant_block<D, ROTATE, false>(q, w - 2 * nkv);
   }
 }
 
@@ -598,22 +617,21 @@ hipError_t launch_d(const Fp8Args& a, hipStream_t stream) {
   int* ev = (int*)(ws + L.ev);
   (void)Np;
   const bool rot = a.signs != nullptr;
-  auto quant = [&](const void* x, int heads, uint8_t* out, int* exps, bool rotate, bool vt) {
-    QuantArgs qa{(const uint16_t*)x, a.signs, out, exps, heads, a.seqlen, nblk};
-    const size_t blocks = (size_t)a.batch * heads * nblk;
-    if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
-    if (vt)
-      hipLaunchKernelGGL((fp8_quant_kernel<D, false, true>), dim3((unsigned)blocks), dim3(256), 0, stream, qa);
-    else if (rotate)
-      hipLaunchKernelGGL((fp8_quant_kernel<D, true, false>), dim3((unsigned)blocks), dim3(256), 0, stream, qa);
-    else
-      hipLaunchKernelGGL((fp8_quant_kernel<D, false, false>), dim3((unsigned)blocks), dim3(256), 0, stream, qa);
-    return hipGetLastError();
-  };
-  hipError_t e;
-  if ((e = quant(a.q, a.heads, q8, eq, rot, false)) != hipSuccess) return e;
-  if ((e = quant(a.k, a.kv_heads, k8, ek, rot, false)) != hipSuccess) return e;
-  if ((e = quant(a.v, a.kv_heads, v8t, ev, false, true)) != hipSuccess) return e;
+  {
+    const QuantArgs qa{(const uint16_t*)a.q, a.signs, q8, eq, a.heads, a.seqlen, nblk};
+    const QuantArgs ka{(const uint16_t*)a.k, a.signs, k8, ek, a.kv_heads, a.seqlen, nblk};
+    const QuantArgs va{(const uint16_t*)a.v, a.signs, v8t, ev, a.kv_heads, a.seqlen, nblk};
+    const size_t nq = (size_t)a.batch * a.heads * nblk, nkv = (size_t)a.batch * a.kv_heads * nblk;
+    if (nq + 2 * nkv > 0x7fffffffu) return hipErrorInvalidConfiguration;
+    if (nq + 2 * nkv > 0) {
+      if (rot)
+        hipLaunchKernelGGL((fp8_quant_qkv_kernel<D, true>), dim3((unsigned)(nq + 2 * nkv)), dim3(256), 0, stream, qa, ka, va, (int)nkv);
+      else
+        hipLaunchKernelGGL((fp8_quant_qkv_kernel<D, false>), dim3((unsigned)(nq + 2 * nkv)), dim3(256), 0, stream, qa, ka, va, (int)nkv);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
 
   AttnArgs p;
   p.q8 = q8;
