@@ -7,8 +7,9 @@
 //     d = 128 eight waves of 32 rows (one workgroup per CU), for d = 64 four waves of 64 rows
 //     (two workgroups per CU, each with its own barriers); the query block stays in
 //     registers while 32-key blocks of K and V stream through LDS and are shared by the
-//     workgroup's waves (three buffers each, every copy issued two steps before the step
-//     that reads it, so no step waits for its own copies; two with a sliding window);
+//     workgroup's waves (four buffers each: every other step copies the tiles of the next
+//     pair of steps, and the workgroup synchronises once per pair; with a sliding window two
+//     buffers and a barrier every step);
 //   * each wave owns whole query rows, so the running max, running sum and output
 //     accumulator of a row never leave the wave (NG = kQW / 32 query groups per wave, each
 //     K or V operand read from LDS feeding NG MFMAs);
@@ -156,38 +157,37 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64, 2) void fwd_bf16_kernel(FwdKe
   constexpr int LOADS = TILE_B / 1024 / CPW;
   static_assert(TILE_B % (1024 * CPW) == 0, "tile must split evenly over the copying waves");
   static_assert(KS == 2, "the score layout below assumes 32-key blocks");
-  // K and V tile buffers each: three (a copy is issued two steps before the step that reads
-  // it, so a step never waits for its own copies), two with a window (waves start at
-  // different blocks, so the three-buffer rotation would need a run-time phase: see the loop)
-  constexpr int NBUF = WINDOW ? 2 : 3;
-  // copies of the current step a wave leaves in flight at the end of a step
-  constexpr int INFLIGHT = NBUF == 3 ? 2 * LOADS : 0;
+  // K and V tile buffers each: four (steps go in pairs with one barrier a pair: the even
+  // step of a pair copies the four tiles the next pair reads, a step ahead of the wait for
+  // them), two with a window (waves start at different blocks, so the four-buffer rotation
+  // would need a run-time phase: see the loop)
+  constexpr int NBUF = WINDOW ? 2 : 4;
 
   // K and V tiles as separate LDS objects: every access names its buffer at compile time,
   // so the compiler can tell a copy into one buffer from reads of another and does not make
   // those reads wait for the copy.
   __shared__ __attribute__((aligned(1024))) char k_lds0[TILE_B];
   __shared__ __attribute__((aligned(1024))) char k_lds1[TILE_B];
-  __shared__ __attribute__((aligned(1024))) char k_lds2[NBUF == 3 ? TILE_B : 16];
+  __shared__ __attribute__((aligned(1024))) char k_lds2[NBUF == 4 ? TILE_B : 16];
+  __shared__ __attribute__((aligned(1024))) char k_lds3[NBUF == 4 ? TILE_B : 16];
   __shared__ __attribute__((aligned(1024))) char v_lds0[TILE_B];
   __shared__ __attribute__((aligned(1024))) char v_lds1[TILE_B];
-  __shared__ __attribute__((aligned(1024))) char v_lds2[NBUF == 3 ? TILE_B : 16];
+  __shared__ __attribute__((aligned(1024))) char v_lds2[NBUF == 4 ? TILE_B : 16];
+  __shared__ __attribute__((aligned(1024))) char v_lds3[NBUF == 4 ? TILE_B : 16];
   auto kbuf = [&](auto bc) -> char* {
     constexpr int b = decltype(bc)::value % NBUF;
-    return b == 0 ? k_lds0 : (b == 1 ? k_lds1 : k_lds2);
+    return b == 0 ? k_lds0 : (b == 1 ? k_lds1 : (b == 2 ? k_lds2 : k_lds3));
   };
   auto vbuf = [&](auto bc) -> char* {
     constexpr int b = decltype(bc)::value % NBUF;
-    return b == 0 ? v_lds0 : (b == 1 ? v_lds1 : v_lds2);
+    return b == 0 ? v_lds0 : (b == 1 ? v_lds1 : (b == 2 ? v_lds2 : v_lds3));
   };
-  // Workgroup barrier once this wave's copies other than the INFLIGHT most recent ones have
-  // landed (and, with LGKM, its LDS stores). __syncthreads() would wait for every copy: its
-  // workgroup-scope release fence waits for all outstanding copies into LDS. The
-  // wavefront-scope fences emit nothing; they keep the compiler from moving memory accesses
-  // across the barrier.
+  // Workgroup barrier once this wave's copies into LDS (and, with LGKM, its LDS stores) have
+  // landed. The wavefront-scope fences emit nothing; they keep the compiler from moving
+  // memory accesses across the barrier.
   auto sync_copies = [](auto lgkmc) {
     constexpr int lgkm = decltype(lgkmc)::value ? 0 : 0xF00;  // lgkmcnt(0), or no LGKM wait
-    __builtin_amdgcn_s_waitcnt(0x70 | lgkm | INFLIGHT);      // vmcnt(INFLIGHT), no EXP wait
+    __builtin_amdgcn_s_waitcnt(0x70 | lgkm);                  // vmcnt(0), no EXP wait
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -550,14 +550,14 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64, 2) void fwd_bf16_kernel(FwdKe
     using KT = std::integral_constant<bool, true>;
     using VT = std::integral_constant<bool, false>;
 
-    // ---- prologue: K(0) .. K(NBUF-1) -> K buffers 0 .. NBUF-1 (and with three buffers
-    // V(0) -> V buffer 0, issued last); V buffer NBUF-1 is cleared so the first step's P V (a
-    // zero P block times that buffer) adds exact zeros. A block whose rows see no key at all
-    // skips to the epilogue (zeros, LSE -inf).
+    // ---- prologue: K(0), K(1) -> K buffers 0, 1 (and with four buffers K(2) -> K buffer 2,
+    // V(0) -> V buffer 0: the tiles of the first pair of steps); V buffer NBUF-1 is cleared so
+    // the first step's P V (a zero P block times that buffer) adds exact zeros. A block whose
+    // rows see no key at all skips to the epilogue (zeros, LSE -inf).
     if (ntiles > 0) {
     issue(KT(), B0(), 0);
     issue(KT(), B1(), min(1, ntiles - 1));
-    if constexpr (NBUF == 3) {
+    if constexpr (NBUF == 4) {
       issue(KT(), std::integral_constant<int, 2>(), min(2, ntiles - 1));
       issue(VT(), B0(), 0);
     }
@@ -573,7 +573,7 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64, 2) void fwd_bf16_kernel(FwdKe
     for (int g = 0; g < NG; ++g)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) pB[g][ks] = bf16x8{};
-    sync_copies(LgkmToo());  // K(0), K(1) and the cleared buffer are in place
+    sync_copies(LgkmToo());  // the first tiles and the cleared buffer are in place
     if (ws == 0 && wtiles > 0) {
       qk(sA, B0());
 #pragma unroll
@@ -586,15 +586,15 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64, 2) void fwd_bf16_kernel(FwdKe
     }
     sync_copies(VmOnly());  // every wave is done with K(0)
 
-    // ---- step j (phase PH = j % 6 with three buffers, j % 2 with two; tile t lives in
-    // buffer t % NBUF), for j < wtiles:
-    // computes S(j+1) = K(j+1) Q^T, P(j) from S(j), and O += V(j-1) P(j-1); copies
-    // K(j+NBUF) and V(j+NBUF-2) (into the buffers of K(j) and V(j-2), which every wave has
-    // finished with by the previous step's barrier), so a copy lands within the step after
-    // the one that issues it, two steps before it is read with three buffers; ends by waiting
-    // for the copies of the step before (with two buffers: of this step) and a barrier. Past
-    // the last block the loads repeat the last block (its buffer is free and the copy is
-    // never read), so a step has no branches.
+    // ---- step j (phase PH = j % 4 with four buffers, j % 2 with two; tile t lives in
+    // buffer t % NBUF), for j < wtiles: computes S(j+1) = K(j+1) Q^T, P(j) from S(j), and
+    // O += V(j-1) P(j-1). Four buffers: an even step j copies K(j+3), K(j+4), V(j+1), V(j+2)
+    // (into the buffers of K(j-1), K(j), V(j-3), V(j-2), which every wave finished with in the
+    // previous pair) and an odd step j+1 ends the pair: it waits for those copies, issued a
+    // step earlier, and the workgroup synchronises; within a pair no wave writes a buffer
+    // another may still read (K(j+1), K(j+2), V(j-1), V(j)). Two buffers: every step copies
+    // K(j+2), V(j), waits for them and synchronises. Past the last block the copies repeat
+    // the last block (into a free buffer, never read), so a step has no branches.
     //
     // The step is laid out by hand as NSLOT slots, one MFMA each (the score MFMAs first, then
     // those of P V), fenced by scheduling barriers. Each slot also carries a fixed share of
@@ -629,8 +629,23 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64, 2) void fwd_bf16_kernel(FwdKe
     // the copies of step j: K(j+NBUF) -> the buffer of K(j), V(j+NBUF-2) -> that of V(j-2)
     auto issue_step = [&](auto phase, int j) {
       constexpr int PH = decltype(phase)::value;
-      issue(KT(), std::integral_constant<int, PH>(), min(j + NBUF, ntiles - 1));
-      issue(VT(), std::integral_constant<int, PH + NBUF - 2>(), min(j + NBUF - 2, ntiles - 1));
+      if constexpr (NBUF == 4) {
+        if constexpr ((PH & 1) == 0) {  // even steps copy the next pair's tiles
+          issue(KT(), std::integral_constant<int, PH + 3>(), min(j + 3, ntiles - 1));
+          issue(KT(), std::integral_constant<int, PH>(), min(j + 4, ntiles - 1));
+          issue(VT(), std::integral_constant<int, PH + 1>(), min(j + 1, ntiles - 1));
+          issue(VT(), std::integral_constant<int, PH + 2>(), min(j + 2, ntiles - 1));
+        }
+      } else {
+        issue(KT(), std::integral_constant<int, PH>(), min(j + NBUF, ntiles - 1));
+        issue(VT(), std::integral_constant<int, PH + NBUF - 2>(), min(j + NBUF - 2, ntiles - 1));
+      }
+    };
+    // end of step PH: with four buffers only odd steps wait (for the pair's copies) and
+    // synchronize; with two, every step
+    auto end_step = [&](auto phase) {
+      constexpr int PH = decltype(phase)::value;
+      if constexpr (NBUF != 4 || (PH & 1) == 1) sync_copies(VmOnly());
     };
 
     auto step = [&](auto phase, int j) {
@@ -748,12 +763,12 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64, 2) void fwd_bf16_kernel(FwdKe
       }
 #pragma unroll
       for (int g = 0; g < NG; ++g) l_part[g] += bs[g];
-      sync_copies(VmOnly());  // the copies of K(j+2), V(j) have landed
+      end_step(phase);
     };
     // a step of a wave past its last key block: its share of the loads, and the barrier
     auto idle_step = [&](auto phase, int j) {
       issue_step(phase, j);
-      sync_copies(VmOnly());
+      end_step(phase);
     };
     // step j of a wave whose first block is j + 1 (window): that step's loads, then S(j+1),
     // formed as the prologue forms S(0); P(j) is zero
@@ -779,10 +794,11 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64, 2) void fwd_bf16_kernel(FwdKe
     };
     // Every wave runs ntiles steps (the same barriers); it computes blocks ws .. wtiles-1,
     // and the last P block of the wave is multiplied into O right after them. The main loop
-    // runs a whole period of phases a pass (6 steps with three buffers, 2 with two); steps
-    // whose phase is known only at run time (idle steps, the tail) dispatch on it. (A window wave may start at any block:
-    // with three buffers its first steps would need such a dispatch inside the loop, which
-    // made the compiler spill; windows keep two buffers and the two-step loop.)
+    // runs a whole period of phases a pass (4 steps with four buffers, 2 with two); steps
+    // whose phase is known only at run time (idle steps, the tail) dispatch on it. (A window
+    // wave may start at any block: with more buffers its first steps would need such a
+    // dispatch inside the loop, which made the compiler spill; windows keep two buffers and
+    // the two-step loop.)
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
     int j = 0;
@@ -829,16 +845,12 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64, 2) void fwd_bf16_kernel(FwdKe
     } else {
       using P2 = std::integral_constant<int, 2>;
       using P3 = std::integral_constant<int, 3>;
-      using P4 = std::integral_constant<int, 4>;
-      using P5 = std::integral_constant<int, 5>;
       if (computes) {
-        for (; j + 5 < wtiles; j += 6) {
+        for (; j + 3 < wtiles; j += 4) {
           step(P0(), j);
           step(P1(), j + 1);
           step(P2(), j + 2);
           step(P3(), j + 3);
-          step(P4(), j + 4);
-          step(P5(), j + 5);
         }
         if (j < wtiles) {
           step(P0(), j);
@@ -846,35 +858,25 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64, 2) void fwd_bf16_kernel(FwdKe
             step(P1(), j);
             if (++j < wtiles) {
               step(P2(), j);
-              if (++j < wtiles) {
-                step(P3(), j);
-                if (++j < wtiles) {
-                  step(P4(), j);
-                  ++j;
-                }
-              }
+              ++j;
             }
           }
         }
         // the last block wtiles-1: its P is in pA (even) or pB (odd), its V in buffer
-        // (wtiles-1) % 3
-        switch ((wtiles - 1) % 6) {
+        // (wtiles-1) % 4
+        switch ((wtiles - 1) % 4) {
           case 0: pv_tail(pA, P0()); break;
           case 1: pv_tail(pB, P1()); break;
           case 2: pv_tail(pA, P2()); break;
-          case 3: pv_tail(pB, P3()); break;
-          case 4: pv_tail(pA, P4()); break;
-          default: pv_tail(pB, P5()); break;
+          default: pv_tail(pB, P3()); break;
         }
       }
       for (; j < ntiles; ++j) {
-        switch (j % 6) {
+        switch (j % 4) {
           case 0: idle_step(P0(), j); break;
           case 1: idle_step(P1(), j); break;
           case 2: idle_step(P2(), j); break;
-          case 3: idle_step(P3(), j); break;
-          case 4: idle_step(P4(), j); break;
-          default: idle_step(P5(), j); break;
+          default: idle_step(P3(), j); break;
         }
       }
     }
