@@ -166,27 +166,42 @@ def test_fwd_fp8_outlier_accuracy():
     assert rmse_plain > 1.5 * rmse_rot
 
 
-def test_fwd_fp8_full_size_sampled_rows():
-    """B=2, H=16, N=8192, d=128, causal, rotated (the bench's FP8 workload): sampled rows of
-    sampled heads against the emulation (the head's operands quantized whole, the row's
-    online loop over its keys)."""
+def test_fwd_fp8_full_size():
+    """B=2, H=16, N=8192, d=128, causal, rotated (the bench's FP8 workload): the quantized
+    operands of all 32 heads bit-exact against the oracle's rotation and quantization, the
+    first 256 rows of every head element by element against the emulation, and sampled rows
+    further down (the emulation's online loop over each row's keys)."""
     torch = pytest.importorskip("torch")
     B, N, H, d = 2, 8192, 16, 128
     gen = torch.Generator(device="cuda")
     gen.manual_seed(11)
     q, k, v = (torch.randn((B, N, H, d), generator=gen, device="cuda", dtype=torch.bfloat16) for _ in range(3))
     signs = synth.rademacher_signs(11, d)
-    o, lse = fa().fwd_fp8(q, k, v, signs=dev_f32(signs), causal=True)
+    ws = torch.zeros(fa().lib().fa_fwd_fp8_workspace_bytes(B, H, H, N, d), dtype=torch.uint8, device="cuda")
+    o, lse = fa().fwd_fp8(q, k, v, signs=dev_f32(signs), causal=True, workspace=ws)
     o, lse = host(o), host(lse)
+    qg, kg, vg, _ = workspace_operands(ws.cpu().numpy(), B, H, H, N, d)
+    del ws
+    qa, ka, va = host(q), host(k), host(v)
     rng = np.random.default_rng(3)
     worst = 0.0
-    for b, h in ((0, 0), (1, 9)):
-        qh, kh, vh, sc = oracle.fp8_operands(host(q[b, :, h]), host(k[b, :, h]), host(v[b, :, h]), 1 / math.sqrt(d),
-                                             signs)
-        for i in sorted(set([0, 63, 64, 4095, N - 1] + list(rng.integers(0, N, 4)))):
-            o_ref, lse_ref = oracle.fp8_online_attention(qh[i:i + 1], kh[:i + 1], vh[:i + 1], sc, True, row_offset=i)
-            slack, _ = code_slack(qh[i:i + 1], kh[:i + 1], vh[:i + 1], sc, True, row0=i)
-            worst = max(worst, check_elements(o[b, i:i + 1, h], o_ref, slack))
-            assert abs(lse[b, h, i] - lse_ref[0]) <= 1e-3, (b, h, i)
-    print(f"fp8 full size: largest error / bound {worst:.3f}")
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh, sc = oracle.fp8_operands(qa[b, :, h], ka[b, :, h], va[b, :, h], 1 / math.sqrt(d), signs)
+            np.testing.assert_array_equal(qg[b, h], qh)
+            np.testing.assert_array_equal(kg[b, h], kh)
+            np.testing.assert_array_equal(vg[b, h], vh)
+            o_ref, lse_ref = oracle.fp8_online_attention(qh[:256], kh[:256], vh[:256], sc, True)
+            slack, _ = code_slack(qh[:256], kh[:256], vh[:256], sc, True)
+            worst = max(worst, check_elements(o[b, :256, h], o_ref, slack))
+            assert np.max(np.abs(lse[b, h, :256] - lse_ref)) <= 1e-3, (b, h)
+            if (b, h) not in ((0, 0), (1, 9)):
+                continue
+            for i in sorted(set([4095, N - 1] + list(rng.integers(256, N, 4)))):
+                o_ref, lse_ref = oracle.fp8_online_attention(qh[i:i + 1], kh[:i + 1], vh[:i + 1], sc, True,
+                                                             row_offset=i)
+                slack, _ = code_slack(qh[i:i + 1], kh[:i + 1], vh[:i + 1], sc, True, row0=i)
+                worst = max(worst, check_elements(o[b, i:i + 1, h], o_ref, slack))
+                assert abs(lse[b, h, i] - lse_ref[0]) <= 1e-3, (b, h, i)
+    print(f"fp8 full size: codes of all {B * H} heads bit-exact; largest error / bound {worst:.3f}")
     assert np.isfinite(o).all() and np.isfinite(lse).all()
